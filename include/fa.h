@@ -1,0 +1,106 @@
+/*
+ * fa.h — C ABI of the MI355X (gfx950) exact-attention library, libfa.so.
+ *
+ * The library computes exact attention O = softmax(scale · Q Kᵀ) · V with the tiled, IO-aware method:
+ * the N×N scores S and probabilities P exist only as on-chip tiles and are never written to device
+ * memory ("Anatomy of a FlashAttention Kernel", section "Why is attention memory-bound, and how does
+ * FlashAttention fix it?"; "flash attention" glossary entry, comparison table).  The forward streams
+ * key/value tiles with the online softmax (same page, section "What is online softmax and how does
+ * tiling keep it exact?") and keeps one statistic per query row; the backward recomputes S and P tile
+ * by tile from Q, K, V and that statistic (section "How does FlashAttention save memory in the
+ * backward pass?").
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  Layout     Q, K, V, O, dO, dQ, dK, dV are contiguous [B, H, N, d] arrays, d innermost, 16-bit
+ *             elements unless stated; element (b,h,i,t) is at ((b·H + h)·N + i)·d + t.  LSE is a
+ *             contiguous fp32 [B, H, N] array.  Queries and keys share the sequence length N.
+ *  LSE        LSE_i = ln Σ_j exp(scale · q_i·k_j) over the keys query i may use: natural log of the
+ *             scaled scores.  It stands for the pair (row maximum, softmax denominator).
+ *  Causal     causal != 0 lets query i use key j only when j ≤ i; causal == 0 lets it use all keys.
+ *  Supported  d ∈ {64, 128}; N ≥ 1; B, H ≥ 1; B·H·N·d < 2^40.  bf16 values are IEEE bfloat16.
+ *  Memory     Every pointer is a device pointer owned by the caller and 16-byte aligned.  The library
+ *             never allocates or frees device memory and keeps no state between calls.
+ *  Streams    Every call only enqueues work on `stream` and returns; results are ready when the stream
+ *             reaches that point.  Calls are re-entrant and may be made on several streams at once.
+ *  Errors     Arguments are checked before any HIP call; a failed check returns its status and enqueues
+ *             nothing.  A launch failure reported by the HIP runtime returns FA_ERR_LAUNCH.  Faults
+ *             inside a kernel surface at the caller's next synchronisation of the stream.
+ */
+#ifndef FA_H_
+#define FA_H_
+
+#include <stddef.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FA_OK = 0,
+  FA_ERR_NULL = 1,        /* a required pointer is NULL                                   */
+  FA_ERR_SHAPE = 2,       /* B, H or N < 1, or the element count is out of range           */
+  FA_ERR_UNSUPPORTED = 3, /* d not in {64, 128}, or a non-finite / non-positive scale      */
+  FA_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned                              */
+  FA_ERR_WORKSPACE = 5,   /* backward workspace is NULL or smaller than fa_bwd_workspace_bytes */
+  FA_ERR_LAUNCH = 6       /* the HIP runtime rejected a kernel launch                      */
+} fa_status;
+
+/*
+ * Forward pass, bf16 in, bf16 out ("Anatomy of a FlashAttention Kernel", sections "Why is attention
+ * memory-bound ..." and "What is online softmax ...").
+ *   q, k, v   [B,H,N,d] bf16 inputs.
+ *   o         [B,H,N,d] bf16 output, O = softmax(scale · Q Kᵀ) V (fp32 accumulation, rounded once).
+ *   lse       [B,H,N] fp32 output, the per-row logsumexp defined above.
+ *   softmax_scale  multiplier of Q Kᵀ (1/√d for standard attention); finite and > 0.
+ */
+fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                 int B, int H, int N, int d, int causal, float softmax_scale, hipStream_t stream);
+
+/*
+ * Forward pass with FP8 matrix products ("Anatomy ...", section "What changed between FlashAttention
+ * 1, 2, and 3?": low-precision FP8).  Q, K, V are OCP e4m3fn codes with one fp32 scale per tensor:
+ * the value of a code c in tensor X is c · x_descale.  Both products (Q Kᵀ and P V) run on fp8 matrix
+ * cores with fp32 accumulation; P is rounded to e4m3 before P V and the softmax denominator is summed
+ * from those same rounded values.
+ *   q8, k8, v8   [B,H,N,d] e4m3fn codes (1 byte each), 16-byte aligned.
+ *   q_descale, k_descale, v_descale   finite, > 0.
+ *   o            [B,H,N,d] bf16 output;  lse  [B,H,N] fp32 output (natural log, scaled scores).
+ * d must be 128.
+ */
+fa_status fa_fwd_fp8(const void* q8, const void* k8, const void* v8,
+                     float q_descale, float k_descale, float v_descale, void* o, float* lse,
+                     int B, int H, int N, int d, int causal, float softmax_scale, hipStream_t stream);
+
+/*
+ * Bytes of device workspace fa_bwd needs for a shape: an fp32 [B,H,N,d] accumulator for dQ plus an
+ * fp32 [B,H,N] array for D_i = dO_i · O_i, each rounded up to 256 bytes.  Returns 0 for an
+ * unsupported shape.
+ */
+size_t fa_bwd_workspace_bytes(int B, int H, int N, int d);
+
+/*
+ * Backward pass ("Anatomy ...", section "How does FlashAttention save memory in the backward pass?"):
+ * recomputes the score and probability tiles from q, k, v and lse and produces the gradients of
+ * O = softmax(scale · Q Kᵀ) V for the upstream gradient dout.
+ *   q, k, v, o, dout  [B,H,N,d] bf16 inputs (o and lse as returned by fa_fwd for the same inputs).
+ *   lse               [B,H,N] fp32 input.
+ *   dq, dk, dv        [B,H,N,d] bf16 outputs (fp32 accumulation, rounded once).
+ *   workspace         device scratch of at least fa_bwd_workspace_bytes(B,H,N,d) bytes, 256-byte
+ *                     aligned, owned by the caller; its contents on entry do not matter and on return
+ *                     are unspecified.  It must not be shared by calls in flight at the same time.
+ * The low bits of dq may differ from run to run (dQ is summed with atomic adds in unspecified order).
+ */
+fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                 const void* dout, void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                 int B, int H, int N, int d, int causal, float softmax_scale, hipStream_t stream);
+
+/* A static, human-readable name for a status code (never NULL). */
+const char* fa_status_str(fa_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H_ */

@@ -1,0 +1,163 @@
+"""Python binding of libfa.so, the gfx950 exact-attention library (C ABI in include/fa.h).
+
+Argument marshalling only: every step of the computation runs in the library's HIP kernels.  PyTorch
+supplies device memory (``torch.empty``) and the current HIP stream; tensors must be contiguous
+[B, H, N, d] on a ROCm device.  There is no fallback: if the library is missing or a call fails, an
+exception is raised.
+
+Entry points (same names as the C ABI, without the ``fa_`` prefix):
+  fwd(q, k, v, causal, scale=None) -> (o, lse)
+  fwd_fp8(q8, k8, v8, q_descale, k_descale, v_descale, causal, scale=None) -> (o, lse)
+  bwd(q, k, v, o, lse, dout, causal, scale=None, workspace=None) -> (dq, dk, dv)
+  bwd_workspace_bytes(B, H, N, d) -> int
+  status_str(code) -> str
+"""
+
+import ctypes
+import math
+import os
+
+import torch
+
+__all__ = ["fwd", "fwd_fp8", "bwd", "bwd_workspace_bytes", "status_str", "FaError", "library",
+           "LIB_PATH"]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
+
+FA_OK = 0
+_STATUS = {0: "FA_OK", 1: "FA_ERR_NULL", 2: "FA_ERR_SHAPE", 3: "FA_ERR_UNSUPPORTED",
+           4: "FA_ERR_ALIGN", 5: "FA_ERR_WORKSPACE", 6: "FA_ERR_LAUNCH"}
+
+_lib = None
+
+
+class FaError(RuntimeError):
+    """A libfa entry point returned a status other than FA_OK."""
+
+    def __init__(self, fn, code, message):
+        super().__init__(f"{fn} failed with status {code} ({message})")
+        self.code = code
+
+
+def library():
+    """Load libfa.so (after torch, so it binds to the HIP runtime torch already loaded)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is not built; run `python -m io_aware_exact_18_amd.build` first")
+        lib = ctypes.CDLL(LIB_PATH)
+        vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+        lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, vp]
+        lib.fa_fwd.restype = i
+        lib.fa_fwd_fp8.argtypes = [vp, vp, vp, f, f, f, vp, vp, i, i, i, i, i, f, vp]
+        lib.fa_fwd_fp8.restype = i
+        lib.fa_bwd_workspace_bytes.argtypes = [i, i, i, i]
+        lib.fa_bwd_workspace_bytes.restype = sz
+        lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, f, vp]
+        lib.fa_bwd.restype = i
+        lib.fa_status_str.argtypes = [i]
+        lib.fa_status_str.restype = ctypes.c_char_p
+        _lib = lib
+    return _lib
+
+
+def status_str(code):
+    return library().fa_status_str(int(code)).decode()
+
+
+def _check(fn, code):
+    if code != FA_OK:
+        raise FaError(fn, code, status_str(code))
+
+
+def _require(t, name, dtype, shape=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a ROCm device, got {t.device}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _scale(scale, d):
+    return 1.0 / math.sqrt(d) if scale is None else float(scale)
+
+
+def fwd(q, k, v, causal, scale=None):
+    """Forward pass: returns (o bf16 [B,H,N,d], lse fp32 [B,H,N])."""
+    _require(q, "q", torch.bfloat16)
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, N, d]")
+    _require(k, "k", torch.bfloat16, q.shape)
+    _require(v, "v", torch.bfloat16, q.shape)
+    B, H, N, d = q.shape
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    with torch.cuda.device(q.device):
+        code = library().fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                lse.data_ptr(), B, H, N, d, int(bool(causal)), _scale(scale, d),
+                                _stream(q.device))
+    _check("fa_fwd", code)
+    return o, lse
+
+
+def fwd_fp8(q8, k8, v8, q_descale, k_descale, v_descale, causal, scale=None):
+    """FP8 forward: e4m3fn codes with per-tensor descales in; (o bf16, lse fp32) out."""
+    _require(q8, "q8", torch.float8_e4m3fn)
+    if q8.dim() != 4:
+        raise ValueError("q8 must be [B, H, N, d]")
+    _require(k8, "k8", torch.float8_e4m3fn, q8.shape)
+    _require(v8, "v8", torch.float8_e4m3fn, q8.shape)
+    B, H, N, d = q8.shape
+    o = torch.empty((B, H, N, d), dtype=torch.bfloat16, device=q8.device)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q8.device)
+    with torch.cuda.device(q8.device):
+        code = library().fa_fwd_fp8(q8.data_ptr(), k8.data_ptr(), v8.data_ptr(), float(q_descale),
+                                    float(k_descale), float(v_descale), o.data_ptr(),
+                                    lse.data_ptr(), B, H, N, d, int(bool(causal)),
+                                    _scale(scale, d), _stream(q8.device))
+    _check("fa_fwd_fp8", code)
+    return o, lse
+
+
+def bwd_workspace_bytes(B, H, N, d):
+    return int(library().fa_bwd_workspace_bytes(B, H, N, d))
+
+
+def bwd(q, k, v, o, lse, dout, causal, scale=None, workspace=None):
+    """Backward pass: returns (dq, dk, dv), bf16 [B,H,N,d].
+
+    ``workspace`` is an optional preallocated uint8 device tensor of at least
+    ``bwd_workspace_bytes(B, H, N, d)`` bytes; without it one is allocated per call.
+    """
+    _require(q, "q", torch.bfloat16)
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, N, d]")
+    for t, name in ((k, "k"), (v, "v"), (o, "o"), (dout, "dout")):
+        _require(t, name, torch.bfloat16, q.shape)
+    B, H, N, d = q.shape
+    _require(lse, "lse", torch.float32, (B, H, N))
+    need = bwd_workspace_bytes(B, H, N, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    else:
+        _require(workspace, "workspace", torch.uint8)
+    dq = torch.empty_like(q)
+    dk = torch.empty_like(q)
+    dv = torch.empty_like(q)
+    with torch.cuda.device(q.device):
+        code = library().fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                lse.data_ptr(), dout.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                                dv.data_ptr(), workspace.data_ptr(), workspace.numel(), B, H, N, d,
+                                int(bool(causal)), _scale(scale, d), _stream(q.device))
+    _check("fa_bwd", code)
+    return dq, dk, dv

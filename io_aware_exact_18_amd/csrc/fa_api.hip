@@ -1,0 +1,101 @@
+// fa_api.hip — the extern "C" entry points declared in include/fa.h: argument checks, then launches.
+//
+// Every check runs before any HIP call, so a rejected call enqueues nothing and needs no GPU.
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/fa.h"
+#include "fa_launch.h"
+
+namespace {
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+// Shape limits: per-head tensors are addressed with 32-bit byte offsets by the kernels' buffer loads
+// (one extra tile of headroom), grids are 32-bit, and B·H·N·d stays below 2^40.
+fa_status check_shape(int B, int H, int N, int d, size_t elem_bytes) {
+  if (B < 1 || H < 1 || N < 1) return FA_ERR_SHAPE;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  const uint64_t per_head = (uint64_t)(N + 256) * (uint64_t)d * elem_bytes;
+  if (per_head >= (1ull << 31)) return FA_ERR_SHAPE;
+  const uint64_t total = (uint64_t)B * (uint64_t)H * (uint64_t)N * (uint64_t)d;
+  if (total >= (1ull << 40)) return FA_ERR_SHAPE;
+  if ((uint64_t)B * (uint64_t)H * (uint64_t)((N + 63) / 64) >= (1ull << 31)) return FA_ERR_SHAPE;
+  return FA_OK;
+}
+
+bool good_scale(float s) { return isfinite(s) && s > 0.f; }
+
+}  // namespace
+
+extern "C" {
+
+const char* fa_status_str(fa_status status) {
+  switch (status) {
+    case FA_OK: return "FA_OK";
+    case FA_ERR_NULL: return "FA_ERR_NULL: a required pointer is NULL";
+    case FA_ERR_SHAPE: return "FA_ERR_SHAPE: B, H or N out of range";
+    case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: head dimension, scale or descale not supported";
+    case FA_ERR_ALIGN: return "FA_ERR_ALIGN: a pointer is not suitably aligned";
+    case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE: backward workspace missing or too small";
+    case FA_ERR_LAUNCH: return "FA_ERR_LAUNCH: the HIP runtime rejected a kernel launch";
+  }
+  return "unknown fa_status";
+}
+
+fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                 int N, int d, int causal, float softmax_scale, hipStream_t stream) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+  fa_status st = check_shape(B, H, N, d, 2);
+  if (st != FA_OK) return st;
+  if (!good_scale(softmax_scale)) return FA_ERR_UNSUPPORTED;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 16))
+    return FA_ERR_ALIGN;
+  fa::FwdArgs a{q, k, v, o, lse, B, H, N, d, causal ? 1 : 0, softmax_scale};
+  return fa::launch_fwd_bf16(a, stream) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+fa_status fa_fwd_fp8(const void* q8, const void* k8, const void* v8, float q_descale,
+                     float k_descale, float v_descale, void* o, float* lse, int B, int H, int N,
+                     int d, int causal, float softmax_scale, hipStream_t stream) {
+  if (!q8 || !k8 || !v8 || !o || !lse) return FA_ERR_NULL;
+  fa_status st = check_shape(B, H, N, d, 2);
+  if (st != FA_OK) return st;
+  if (d != 128) return FA_ERR_UNSUPPORTED;
+  if (!good_scale(softmax_scale) || !good_scale(q_descale) || !good_scale(k_descale) ||
+      !good_scale(v_descale))
+    return FA_ERR_UNSUPPORTED;
+  if (!aligned(q8, 16) || !aligned(k8, 16) || !aligned(v8, 16) || !aligned(o, 16) ||
+      !aligned(lse, 16))
+    return FA_ERR_ALIGN;
+  fa::Fp8FwdArgs a{q8, k8, v8, q_descale, k_descale, v_descale, o, lse,
+                   B, H, N, d, causal ? 1 : 0, softmax_scale};
+  return fa::launch_fwd_fp8(a, stream) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+size_t fa_bwd_workspace_bytes(int B, int H, int N, int d) {
+  if (check_shape(B, H, N, d, 2) != FA_OK) return 0;
+  return fa::bwd_dq_acc_bytes(B, H, N, d) + fa::bwd_delta_bytes(B, H, N);
+}
+
+fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                 const void* dout, void* dq, void* dk, void* dv, void* workspace,
+                 size_t workspace_bytes, int B, int H, int N, int d, int causal,
+                 float softmax_scale, hipStream_t stream) {
+  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return FA_ERR_NULL;
+  fa_status st = check_shape(B, H, N, d, 2);
+  if (st != FA_OK) return st;
+  if (!good_scale(softmax_scale)) return FA_ERR_UNSUPPORTED;
+  if (!workspace || workspace_bytes < fa_bwd_workspace_bytes(B, H, N, d)) return FA_ERR_WORKSPACE;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+      !aligned(lse, 16) || !aligned(dout, 16) || !aligned(dq, 16) || !aligned(dk, 16) ||
+      !aligned(dv, 16) || !aligned(workspace, 256))
+    return FA_ERR_ALIGN;
+  float* dq_acc = (float*)workspace;
+  float* delta = (float*)((char*)workspace + fa::bwd_dq_acc_bytes(B, H, N, d));
+  fa::BwdArgs a{q, k, v, o, lse, dout, dq, dk, dv, dq_acc, delta,
+                B, H, N, d, causal ? 1 : 0, softmax_scale};
+  return fa::launch_bwd_bf16(a, stream) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+}  // extern "C"

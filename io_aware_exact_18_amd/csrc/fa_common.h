@@ -1,0 +1,105 @@
+// fa_common.h — device-side building blocks shared by the gfx950 attention kernels.
+//
+// Matrix-core conventions (measured on gfx950 with a lane-layout probe):
+//   v_mfma_f32_32x32x16_bf16  A is 32×16, B is 16×32, C/D is 32×32 fp32.
+//     A operand: lane l holds row (l % 32) and 8 k-slots; B operand: lane l holds column (l % 32) and
+//     the same 8 k-slots.  Slot e of lane group g = l / 32 is k = 8·g + e (any k order works as long
+//     as A and B agree, which they do by construction here).
+//     D: lane l, register r holds row 8·(r/4) + 4·(l/32) + (r % 4), column l % 32.
+//   ds_read_b64_tr_b16: within each group of 16 lanes, lane i = 4a + b supplies the address of 4
+//     consecutive 16-bit elements M[k0 + a][n0 + 4b .. n0 + 4b + 3] of a row-major LDS matrix; lane
+//     j of the group then receives M[k0 .. k0 + 3][n0 + j], i.e. four consecutive rows of one column.
+//     This feeds a matrix-core operand whose contraction index runs along the rows of M.
+//   Workgroups are dispatched to the 8 XCDs round-robin: block b runs on XCD b % 8.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr uint32_t kBufferFlags = 0x00020000u;  // gfx9 raw buffer: 32-bit data format, no swizzle
+
+// A raw buffer resource over [base, base + bytes).  Loads past `bytes` return zeros, which is how
+// ragged sequence tails are read without branches.
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           (int)kBufferFlags);
+}
+
+__device__ inline u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0);
+}
+
+__device__ inline u32x2 buf_load8(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  return __builtin_amdgcn_raw_buffer_load_b64(r, byte_off, 0, 0);
+}
+
+__device__ inline uint32_t buf_load4(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, byte_off, 0, 0);
+}
+
+__device__ inline f32x16 mfma_32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Four consecutive rows of one column of a row-major bf16 LDS matrix (see the header comment).
+__device__ inline u32x2 lds_read_tr16(const bf16* p) {
+  i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(p));
+  return __builtin_bit_cast(u32x2, r);
+}
+
+// x from this lane and from lane (l ^ 32), combined with max / sum.  Both halves of the wave get a
+// bitwise-identical result.
+__device__ inline float halves_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ inline float halves_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ inline float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Round two floats to bf16 (round-to-nearest-even) and pack them, first in the low half.
+__device__ inline uint32_t pack_bf16x2(float lo, float hi) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  bf16x2_t v;
+  v[0] = (__bf16)lo;
+  v[1] = (__bf16)hi;
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ inline float bf16_bits_to_float(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
+
+// LDS tile layout for a [rows][D] bf16 tile with no padding: the 16-byte chunk c of row r is stored at
+// chunk c ^ f(r), f(r) = ((r & 3) << 1) | ((r >> 2) & 1).  With 32 four-byte banks this keeps both
+// access patterns the kernels use conflict-free: 8 lanes reading 16 bytes from 8 consecutive rows of
+// one chunk, and 16 lanes of a transposed read covering 4 consecutive rows × 32 bytes.
+__device__ inline int swz_f(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
+template <int D>
+__device__ inline int tile_off(int row, int col) {
+  return row * D + ((((col >> 3) ^ swz_f(row)) << 3) | (col & 7));
+}
+
+// blockIdx → logical work item such that consecutive logical items land on the same XCD: logical
+// item L runs on XCD L / (total / 8).  Used only when total is a multiple of 8.
+__device__ inline uint32_t xcd_remap(uint32_t bid, uint32_t total) {
+  return (bid % 8u) * (total / 8u) + bid / 8u;
+}
+
+}  // namespace fa

@@ -1,0 +1,117 @@
+"""C-ABI checks that need no GPU: libfa.so loads, exports every entry point include/fa.h declares,
+and rejects bad arguments with the documented status before any HIP call is made."""
+
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+LIB = os.path.join(ROOT, "io_aware_exact_18_amd", "libfa.so")
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+OK, NULL, SHAPE, UNSUP, ALIGN, WORKSPACE, LAUNCH = range(7)
+P = 0x100000          # a 256-byte-aligned stand-in address; never dereferenced (checks fail first)
+MIS = 0x100008        # not 16-byte aligned
+
+
+@pytest.fixture(scope="module")
+def lib():
+    assert os.path.exists(LIB), "libfa.so is not built (python -m io_aware_exact_18_amd.build)"
+    lib = ctypes.CDLL(LIB)
+    vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, vp]
+    lib.fa_fwd_fp8.argtypes = [vp, vp, vp, f, f, f, vp, vp, i, i, i, i, i, f, vp]
+    lib.fa_bwd_workspace_bytes.argtypes = [i, i, i, i]
+    lib.fa_bwd_workspace_bytes.restype = sz
+    lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, f, vp]
+    lib.fa_status_str.argtypes = [i]
+    lib.fa_status_str.restype = ctypes.c_char_p
+    return lib
+
+
+def test_exports_match_header(lib):
+    text = open(HEADER).read()
+    declared = set(re.findall(r"^\s*(?:fa_status|size_t|const char\*)\s+(fa_\w+)\s*\(", text, re.M))
+    assert declared == {"fa_fwd", "fa_fwd_fp8", "fa_bwd_workspace_bytes", "fa_bwd", "fa_status_str"}
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(lib):
+    for code in range(7):
+        s = lib.fa_status_str(code).decode()
+        assert s.startswith(["FA_OK", "FA_ERR_NULL", "FA_ERR_SHAPE", "FA_ERR_UNSUPPORTED",
+                             "FA_ERR_ALIGN", "FA_ERR_WORKSPACE", "FA_ERR_LAUNCH"][code])
+    assert lib.fa_status_str(99) is not None
+
+
+def fwd(lib, q=P, k=P, v=P, o=P, lse=P, B=1, H=1, N=64, d=64, causal=0, scale=0.125):
+    return lib.fa_fwd(q, k, v, o, lse, B, H, N, d, causal, scale, None)
+
+
+def test_fwd_rejections(lib):
+    assert fwd(lib, q=None) == NULL
+    assert fwd(lib, lse=None) == NULL
+    assert fwd(lib, B=0) == SHAPE
+    assert fwd(lib, H=-1) == SHAPE
+    assert fwd(lib, N=0) == SHAPE
+    assert fwd(lib, d=96) == UNSUP
+    assert fwd(lib, d=32) == UNSUP
+    assert fwd(lib, d=256) == UNSUP
+    for bad in (0.0, -0.5, math.inf, math.nan):
+        assert fwd(lib, scale=bad) == UNSUP
+    assert fwd(lib, v=MIS) == ALIGN
+    assert fwd(lib, o=MIS) == ALIGN
+    assert fwd(lib, N=1 << 23, d=128) == SHAPE           # per-head bytes past the 32-bit offsets
+    assert fwd(lib, B=1 << 16, H=1 << 16, N=1 << 8) == SHAPE  # B·H·N·d ≥ 2^40
+
+
+def fwd8(lib, d=128, qs=1.0, ks=1.0, vs=1.0, k8=P, scale=0.09):
+    return lib.fa_fwd_fp8(P, k8, P, qs, ks, vs, P, P, 1, 1, 64, d, 1, scale, None)
+
+
+def test_fwd_fp8_rejections(lib):
+    assert fwd8(lib, k8=None) == NULL
+    assert fwd8(lib, d=64) == UNSUP
+    assert fwd8(lib, qs=0.0) == UNSUP
+    assert fwd8(lib, vs=math.nan) == UNSUP
+    assert fwd8(lib, scale=-1.0) == UNSUP
+    assert fwd8(lib, k8=MIS) == ALIGN
+
+
+def test_workspace_bytes(lib):
+    def up(x):
+        return (x + 255) // 256 * 256
+    for B, H, N, d in ((1, 1, 1, 64), (8, 16, 2048, 64), (4, 32, 4096, 128), (1, 3, 17, 128)):
+        assert lib.fa_bwd_workspace_bytes(B, H, N, d) == up(B * H * N * d * 4) + up(B * H * N * 4)
+    assert lib.fa_bwd_workspace_bytes(1, 1, 64, 96) == 0
+    assert lib.fa_bwd_workspace_bytes(0, 1, 64, 64) == 0
+
+
+def bwd(lib, ws=P, ws_bytes=None, dq=P, N=64, d=64, scale=0.125, lse=P):
+    if ws_bytes is None:
+        ws_bytes = lib.fa_bwd_workspace_bytes(1, 1, N, d)
+    return lib.fa_bwd(P, P, P, P, lse, P, dq, P, P, ws, ws_bytes, 1, 1, N, d, 0, scale, None)
+
+
+def test_bwd_rejections(lib):
+    assert bwd(lib, dq=None) == NULL
+    assert bwd(lib, lse=None) == NULL
+    assert bwd(lib, N=0) == SHAPE
+    assert bwd(lib, d=80) == UNSUP
+    assert bwd(lib, scale=math.inf) == UNSUP
+    assert bwd(lib, ws=None) == WORKSPACE
+    assert bwd(lib, ws_bytes=1024) == WORKSPACE
+    assert bwd(lib, ws=P + 16) == ALIGN       # workspace needs 256-byte alignment
+    assert bwd(lib, dq=MIS) == ALIGN
+
+
+def test_binding_fails_loudly_without_tensors_on_gpu():
+    import torch
+    import io_aware_exact_18_amd as fa
+    q = torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16)  # a CPU tensor: rejected, no fallback
+    with pytest.raises(ValueError):
+        fa.fwd(q, q, q, causal=False)

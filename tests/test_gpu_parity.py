@@ -1,0 +1,306 @@
+"""GPU parity of the HIP path (through the C ABI) against the fp64 CPU oracle.
+
+Tolerances (bf16 inputs, fp32 accumulation): O max-abs ≤ 1e-2, LSE max-abs ≤ 1e-3, dQ/dK/dV relative
+Frobenius error ≤ 2e-2.  For the long-sequence workload the O bound is read as
+|O − O*| ≤ 1e-2 + ½ ulp_bf16(O*) elementwise: the output is stored in bf16, and where the enlarged
+keys dominate a row |O| reaches [4, 8), whose half-ulp (1/64) alone exceeds 1e-2.
+
+Inputs are the seeded workloads of ``workloads`` at reduced and full sizes; where the oracle would
+take too long at full size, it checks a fixed sample of heads (first, last and two seeded) and every
+head is checked with size-independent properties instead.
+"""
+
+import math
+import random
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+O_TOL, LSE_TOL, GRAD_TOL = 1e-2, 1e-3, 2e-2
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a ROCm device"
+    import io_aware_exact_18_amd as fa
+    fa.library()  # fail loudly if libfa.so is missing
+    yield
+
+
+def fa():
+    import io_aware_exact_18_amd as m
+    return m
+
+
+def _np64(t):
+    return t.detach().to("cpu", torch.float64).numpy()
+
+
+def _sample_heads(bh, k=4, seed=0):
+    heads = {0, bh - 1}
+    rnd = random.Random(seed)
+    while len(heads) < min(k, bh):
+        heads.add(rnd.randrange(bh))
+    return sorted(heads)
+
+
+def _rel_fro(got, ref):
+    den = np.linalg.norm(ref)
+    return np.linalg.norm(got - ref) / (den if den > 0 else 1.0)
+
+
+def _half_ulp_bf16(x):
+    ax = np.abs(x)
+    e = np.floor(np.log2(np.where(ax > 0, ax, 1.0)))
+    return np.where(ax > 0, 2.0 ** (e - 8), 2.0 ** -134)
+
+
+def _run_fwd(q, k, v, causal, scale):
+    dev = "cuda"
+    o, lse = fa().fwd(q.to(dev), k.to(dev), v.to(dev), causal, scale)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+def _check_fwd_heads(q, k, v, o, lse, causal, scale, heads=None, o_tol=None):
+    B, H, N, d = q.shape
+    heads = range(B * H) if heads is None else heads
+    qf, kf, vf = (x.reshape(B * H, N, d) for x in (q, k, v))
+    of = o.reshape(B * H, N, d)
+    lf = lse.reshape(B * H, N)
+    worst_o = worst_l = 0.0
+    for h in heads:
+        o_ref, l_ref = oracle.attention_head_fwd64(_np64(qf[h]), _np64(kf[h]), _np64(vf[h]),
+                                                   causal, scale)
+        og, lg = _np64(of[h]), _np64(lf[h])
+        assert np.all(np.isfinite(og)) and np.all(np.isfinite(lg))
+        err = np.abs(og - o_ref)
+        if o_tol == "bf16_store":
+            assert np.all(err <= O_TOL + _half_ulp_bf16(o_ref)), (h, float(err.max()))
+        else:
+            assert err.max() <= O_TOL, (h, float(err.max()))
+        assert np.abs(lg - l_ref).max() <= LSE_TOL, (h, float(np.abs(lg - l_ref).max()))
+        worst_o = max(worst_o, float(err.max()))
+        worst_l = max(worst_l, float(np.abs(lg - l_ref).max()))
+    return worst_o, worst_l
+
+
+def _run_bwd(q, k, v, do, causal, scale):
+    dev = "cuda"
+    qd, kd, vd, dod = (x.to(dev) for x in (q, k, v, do))
+    o, lse = fa().fwd(qd, kd, vd, causal, scale)
+    dq, dk, dv = fa().bwd(qd, kd, vd, o, lse, dod, causal, scale)
+    torch.cuda.synchronize()
+    return o, lse, dq, dk, dv
+
+
+def _check_bwd_heads(q, k, v, do, dq, dk, dv, causal, scale, heads):
+    B, H, N, d = q.shape
+    flat = [x.reshape(B * H, N, d) for x in (q, k, v, do, dq, dk, dv)]
+    worst = 0.0
+    for h in heads:
+        qh, kh, vh, doh = (_np64(x[h]) for x in flat[:4])
+        ref = oracle.attention_head_bwd64(qh, kh, vh, doh, causal, scale)
+        for got, r, name in zip(flat[4:], ref, ("dq", "dk", "dv")):
+            g = _np64(got[h])
+            assert np.all(np.isfinite(g)), (h, name)
+            e = _rel_fro(g, r)
+            assert e <= GRAD_TOL, (h, name, e)
+            worst = max(worst, e)
+    return worst
+
+
+def _check_bwd_sums(do, dk, dv):
+    """Σ_j dV_j = Σ_i dO_i and Σ_j dK_j = 0 per head (rows of P sum to 1, rows of dS sum to 0)."""
+    sdv = dv.double().sum(dim=2)
+    sdo = do.double().to(dv.device).sum(dim=2)
+    rel = ((sdv - sdo).norm(dim=-1) / sdo.norm(dim=-1).clamp_min(1e-6)).max().item()
+    assert rel <= GRAD_TOL, rel
+    # Σ_j dK_j = 0 up to bf16 rounding of each dK entry: compare with the scale of dK itself.
+    sdk = dk.double().sum(dim=2).norm(dim=-1)
+    mag = dk.double().norm(dim=(2, 3))
+    assert (sdk / mag.clamp_min(1e-12)).max().item() <= GRAD_TOL
+
+
+# ------------------------------------------------------------------------------------------------
+# Forward, small and ragged shapes.
+
+SMALL = [(1, 2, n, d, c) for d in (64, 128) for c in (False, True)
+         for n in (1, 17, 64, 100, 129, 256, 300)]
+
+
+@pytest.mark.parametrize("B,H,N,d,causal", SMALL)
+def test_fwd_small(B, H, N, d, causal):
+    g = torch.Generator().manual_seed(N * 7 + d + int(causal))
+    q, k, v = (torch.randn(B, H, N, d, generator=g).to(torch.bfloat16) for _ in range(3))
+    scale = 1.0 / math.sqrt(d)
+    o, lse = _run_fwd(q, k, v, causal, scale)
+    _check_fwd_heads(q, k, v, o.cpu(), lse.cpu(), causal, scale)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_fwd_equal_scores_closed_form(d, causal):
+    """Q = 0: O_i is the mean of the allowed V rows and LSE_i = ln(#allowed keys)."""
+    N = 200
+    g = torch.Generator().manual_seed(5)
+    q = torch.zeros(1, 2, N, d, dtype=torch.bfloat16)
+    k, v = (torch.randn(1, 2, N, d, generator=g).to(torch.bfloat16) for _ in range(2))
+    o, lse = _run_fwd(q, k, v, causal, 0.1)
+    vv = v.double()
+    if causal:
+        ref = vv.cumsum(dim=2) / torch.arange(1, N + 1, dtype=torch.float64).view(1, 1, N, 1)
+        lref = torch.log(torch.arange(1, N + 1, dtype=torch.float64)).expand(1, 2, N)
+    else:
+        ref = vv.mean(dim=2, keepdim=True).expand_as(vv)
+        lref = torch.full((1, 2, N), math.log(N), dtype=torch.float64)
+    assert (o.cpu().double() - ref).abs().max().item() <= O_TOL
+    assert (lse.cpu().double() - lref).abs().max().item() <= 1e-5
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_fwd_causal_row0_exact(d):
+    """Under the causal mask row 0 sees only key 0: O_0 = V_0 exactly, LSE_0 = scale·q_0·k_0."""
+    g = torch.Generator().manual_seed(11)
+    q, k, v = (torch.randn(2, 3, 77, d, generator=g).to(torch.bfloat16) for _ in range(3))
+    scale = 1.0 / math.sqrt(d)
+    o, lse = _run_fwd(q, k, v, True, scale)
+    assert torch.equal(o[:, :, 0].cpu(), v[:, :, 0])
+    ref = scale * (q[:, :, 0].double() * k[:, :, 0].double()).sum(-1)
+    assert (lse[:, :, 0].cpu().double() - ref).abs().max().item() <= 1e-5
+
+
+def test_fwd_deterministic_and_guarded():
+    """Two runs are bitwise equal, and nothing is written past the end of O or LSE."""
+    B, H, N, d = 2, 3, 333, 128
+    g = torch.Generator().manual_seed(12)
+    q, k, v = (torch.randn(B, H, N, d, generator=g).to(torch.bfloat16).cuda() for _ in range(3))
+    lib = fa().library()
+    n_o, n_l, guard = B * H * N * d, B * H * N, 4096
+    o_buf = torch.full((n_o + guard,), 7.0, dtype=torch.bfloat16, device="cuda")
+    l_buf = torch.full((n_l + guard,), 7.0, dtype=torch.float32, device="cuda")
+    outs = []
+    for _ in range(2):
+        code = lib.fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o_buf.data_ptr(),
+                          l_buf.data_ptr(), B, H, N, d, 1, 1.0 / math.sqrt(d),
+                          torch.cuda.current_stream().cuda_stream)
+        assert code == 0
+        torch.cuda.synchronize()
+        outs.append((o_buf[:n_o].clone(), l_buf[:n_l].clone()))
+        assert bool((o_buf[n_o:] == 7.0).all()) and bool((l_buf[n_l:] == 7.0).all())
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+
+
+# ------------------------------------------------------------------------------------------------
+# Backward, small and ragged shapes.
+
+SMALL_BWD = [(1, 2, n, d, c) for d in (64, 128) for c in (False, True)
+             for n in (1, 17, 100, 129, 256, 300)]
+
+
+@pytest.mark.parametrize("B,H,N,d,causal", SMALL_BWD)
+def test_bwd_small(B, H, N, d, causal):
+    g = torch.Generator().manual_seed(N * 13 + d + int(causal))
+    q, k, v, do = (torch.randn(B, H, N, d, generator=g).to(torch.bfloat16) for _ in range(4))
+    scale = 1.0 / math.sqrt(d)
+    o, lse, dq, dk, dv = _run_bwd(q, k, v, do, causal, scale)
+    _check_fwd_heads(q, k, v, o.cpu(), lse.cpu(), causal, scale)
+    _check_bwd_heads(q, k, v, do, dq.cpu(), dk.cpu(), dv.cpu(), causal, scale, range(B * H))
+
+
+def test_bwd_guarded():
+    """Nothing is written past dQ, dK, dV or the workspace's documented size."""
+    B, H, N, d = 1, 2, 190, 128
+    g = torch.Generator().manual_seed(14)
+    q, k, v, do = (torch.randn(B, H, N, d, generator=g).to(torch.bfloat16).cuda() for _ in range(4))
+    scale = 1.0 / math.sqrt(d)
+    o, lse = fa().fwd(q, k, v, True, scale)
+    lib = fa().library()
+    n, guard = B * H * N * d, 4096
+    bufs = [torch.full((n + guard,), 3.0, dtype=torch.bfloat16, device="cuda") for _ in range(3)]
+    ws_bytes = fa().bwd_workspace_bytes(B, H, N, d)
+    ws = torch.full((ws_bytes + guard,), 0x5A, dtype=torch.uint8, device="cuda")
+    code = lib.fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                      do.data_ptr(), bufs[0].data_ptr(), bufs[1].data_ptr(), bufs[2].data_ptr(),
+                      ws.data_ptr(), ws_bytes, B, H, N, d, 1, scale,
+                      torch.cuda.current_stream().cuda_stream)
+    assert code == 0
+    torch.cuda.synchronize()
+    for b in bufs:
+        assert bool((b[n:] == 3.0).all())
+    assert bool((ws[ws_bytes:] == 0x5A).all())
+    dq, dk, dv = fa().bwd(q, k, v, o, lse, do, True, scale)
+    for b, ref in zip(bufs, (dq, dk, dv)):
+        err = _rel_fro(_np64(b[:n].view(B, H, N, d)), _np64(ref))
+        assert err <= 1e-2
+
+
+# ------------------------------------------------------------------------------------------------
+# The workloads.
+
+def test_workload_fwd_small_full():
+    w = workloads.WORKLOADS["fwd_small"]
+    inp = workloads.make_inputs("fwd_small")
+    o, lse = _run_fwd(inp["q"], inp["k"], inp["v"], w.causal, w.scale)
+    assert tuple(o.shape) == (1, 2, 256, 64) and tuple(lse.shape) == (1, 2, 256)
+    _check_fwd_heads(inp["q"], inp["k"], inp["v"], o.cpu(), lse.cpu(), w.causal, w.scale)
+
+
+@pytest.mark.parametrize("name", ["d64_2k", "causal_4k", "long_16k"])
+def test_workload_reduced(name):
+    """Each backward workload at its own N and d but only 2 heads: every head checked."""
+    w = workloads.WORKLOADS[name]
+    inp = workloads.make_inputs(name, B=1, H=2)
+    o, lse, dq, dk, dv = _run_bwd(inp["q"], inp["k"], inp["v"], inp["do"], w.causal, w.scale)
+    tol = "bf16_store" if w.large_keys else None
+    _check_fwd_heads(inp["q"], inp["k"], inp["v"], o.cpu(), lse.cpu(), w.causal, w.scale,
+                     heads=range(2), o_tol=tol)
+    heads = [0] if w.N > 8192 else range(2)
+    _check_bwd_heads(inp["q"], inp["k"], inp["v"], inp["do"], dq.cpu(), dk.cpu(), dv.cpu(),
+                     w.causal, w.scale, heads)
+
+
+@pytest.mark.parametrize("name", ["d64_2k", "causal_4k"])
+def test_workload_full(name):
+    """Full size, as the bench runs it: sampled heads against the oracle, properties on all heads."""
+    w = workloads.WORKLOADS[name]
+    inp = workloads.make_inputs(name)
+    o, lse, dq, dk, dv = _run_bwd(inp["q"], inp["k"], inp["v"], inp["do"], w.causal, w.scale)
+    for t in (o, lse, dq, dk, dv):
+        assert bool(torch.isfinite(t).all())
+    heads = _sample_heads(w.B * w.H, 4, seed=w.number)
+    _check_fwd_heads(inp["q"], inp["k"], inp["v"], o.cpu(), lse.cpu(), w.causal, w.scale,
+                     heads=heads)
+    _check_bwd_heads(inp["q"], inp["k"], inp["v"], inp["do"], dq.cpu(), dk.cpu(), dv.cpu(),
+                     w.causal, w.scale, heads[:2])
+    _check_bwd_sums(inp["do"], dk, dv)
+
+
+def test_workload_long_full():
+    """Long sequence at full size: sampled rows of every head for the forward, one full head for the
+    backward, properties on all heads."""
+    w = workloads.WORKLOADS["long_16k"]
+    inp = workloads.make_inputs("long_16k")
+    o, lse, dq, dk, dv = _run_bwd(inp["q"], inp["k"], inp["v"], inp["do"], w.causal, w.scale)
+    for t in (o, lse, dq, dk, dv):
+        assert bool(torch.isfinite(t).all())
+    B, H, N, d = w.shape()
+    q, k, v = (inp[x].reshape(B * H, N, d) for x in ("q", "k", "v"))
+    of, lf = o.cpu().reshape(B * H, N, d), lse.cpu().reshape(B * H, N)
+    rnd = random.Random(4)
+    for h in range(B * H):
+        rows = sorted({0, 1, N - 1, 1023, 1024, 8191, 8192} | {rnd.randrange(N) for _ in range(24)})
+        o_ref, l_ref = oracle.attention_rows64(_np64(q[h]), _np64(k[h]), _np64(v[h]), rows, True,
+                                               w.scale)
+        err = np.abs(_np64(of[h][rows]) - o_ref)
+        assert np.all(err <= O_TOL + _half_ulp_bf16(o_ref)), (h, float(err.max()))
+        assert np.abs(_np64(lf[h][rows]) - l_ref).max() <= LSE_TOL
+    _check_bwd_heads(inp["q"], inp["k"], inp["v"], inp["do"], dq.cpu(), dk.cpu(), dv.cpu(),
+                     w.causal, w.scale, [B * H - 1])
+    _check_bwd_sums(inp["do"], dk, dv)
