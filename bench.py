@@ -1,0 +1,247 @@
+#!/usr/bin/env python3
+"""Throughput of exact attention forward + backward on one MI355X, through the C ABI.
+
+One step is one pass of the whole path over one batch: fa_fwd, then the three backward phases
+(fa_bwd_preprocess, fa_bwd_dkdv, fa_bwd_dq), with every input already resident in device memory.
+FLOPs follow the usual convention: forward 4·B·H·N²·d (halved when causal), backward 2.5× the
+forward.  W untimed warm-up steps, then exactly K timed steps between two device
+synchronisations; HIP events on the launch stream give each kernel's own duration.
+
+Prints one JSON line on stdout (progress goes to stderr).  Only one GPU is used: --gpus above 1 is
+refused.  The ``cpu_baseline`` leg times the fp64 CPU oracle on a bounded sample of the same
+workload's heads; it is a reported baseline, not a target.
+"""
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "attention TFLOP/s fwd+bwd (bf16, d=128, N=4096 causal) and % of MFMA peak"
+# MI355X published dense peaks: 256 CUs × 2.4 GHz; bf16 matrix cores 4096 FLOP/clk/CU.
+BF16_PEAK_TFLOPS = 256 * 2.4e9 * 4096 / 1e12     # 2516.6
+HBM_PEAK_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_sha(name):
+    path = os.path.join(ROOT, "io_aware_exact_18_amd", "csrc", name)
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(kernel, src):
+    """HBM bytes per launch from the committed counter summary, if it was taken on this source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    e = t.get(kernel)
+    if not e or e.get("src_sha") != source_sha(src):
+        return None
+    return e.get("bytes_per_launch")
+
+
+def cpu_baseline(w, inp, budget_s):
+    """Time the oracle's forward + backward on whole heads of the workload, up to ~budget_s."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()
+                       if p.get("user_api") == "blas"] or [1])
+    except Exception:  # threadpoolctl missing: report the visible core count
+        threads = os.cpu_count()
+    B, H, N, d = w.shape()
+    flat = {k: inp[k].reshape(B * H, N, d) for k in ("q", "k", "v", "do")}
+    heads, t_total = 0, 0.0
+    while heads < B * H and t_total < budget_s:
+        h = heads
+        q, k, v, do = (flat[x][h].double().numpy() for x in ("q", "k", "v", "do"))
+        t0 = time.perf_counter()
+        oracle.attention_head_fwd64(q, k, v, w.causal, w.scale)
+        oracle.attention_head_bwd64(q, k, v, do, w.causal, w.scale)
+        t_total += time.perf_counter() - t0
+        heads += 1
+    per_head_flops = (w.fwd_flops() + w.bwd_flops()) / (B * H)
+    tflops = heads * per_head_flops / t_total / 1e12
+    return {
+        "value": tflops,
+        "unit": "TFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"fp64 numpy oracle, forward+backward of {heads} of {B * H} heads "
+                  f"(N={N}, d={d}, causal={w.causal}) in {t_total:.1f} s; whole-job time "
+                  f"extrapolated as {B * H / heads:.1f}x (heads are independent and equal in cost)",
+        "seconds_for_sample": t_total,
+        "extrapolated_job_seconds": t_total * B * H / heads,
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="causal_4k",
+                    help="bf16 forward+backward workload (default: the throughput workload)")
+    ap.add_argument("--cpu-budget", type=float, default=15.0,
+                    help="seconds of oracle work for the cpu_baseline leg (0 skips it)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}, WORLD_SIZE {world}); "
+              "attention over heads shards with no communication, so multi-GPU figures are not "
+              "produced here", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import io_aware_exact_18_amd as fa
+    import workloads
+
+    assert torch.cuda.is_available(), "bench.py needs a ROCm device"
+    w = workloads.WORKLOADS[args.workload]
+    if w.fp8 or not w.backward:
+        raise SystemExit("choose a bf16 forward+backward workload")
+    B, H, N, d = w.shape()
+    log(f"[bench] workload {w.name}: B={B} H={H} N={N} d={d} causal={w.causal}")
+    inp = workloads.make_inputs(w.name)
+    dev = torch.device("cuda:0")
+    q, k, v, do = (inp[x].to(dev) for x in ("q", "k", "v", "do"))
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    ws_bytes = fa.bwd_workspace_bytes(B, H, N, d)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    lib = fa.library()
+    stream = torch.cuda.current_stream(dev)
+    sp = stream.cuda_stream
+    causal = int(w.causal)
+    scale = w.scale
+
+    def check(name, code):
+        if code != 0:
+            raise fa.FaError(name, code, fa.status_str(code))
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        check("fa_fwd", lib.fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                   lse.data_ptr(), B, H, N, d, causal, scale, sp))
+        if ev is not None:
+            ev[1].record(stream)
+        check("fa_bwd_preprocess", lib.fa_bwd_preprocess(o.data_ptr(), do.data_ptr(), ws.data_ptr(),
+                                                         ws_bytes, B, H, N, d, sp))
+        if ev is not None:
+            ev[2].record(stream)
+        check("fa_bwd_dkdv", lib.fa_bwd_dkdv(q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                             lse.data_ptr(), do.data_ptr(), dk.data_ptr(),
+                                             dv.data_ptr(), ws.data_ptr(), ws_bytes, B, H, N, d,
+                                             causal, scale, sp))
+        if ev is not None:
+            ev[3].record(stream)
+        check("fa_bwd_dq", lib.fa_bwd_dq(q.data_ptr(), k.data_ptr(), v.data_ptr(), lse.data_ptr(),
+                                         do.data_ptr(), dq.data_ptr(), ws.data_ptr(), ws_bytes, B,
+                                         H, N, d, causal, scale, sp))
+        if ev is not None:
+            ev[4].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize(dev)
+    log(f"[bench] warm-up done ({args.warmup} steps)")
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize(dev)
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize(dev)
+    elapsed = time.perf_counter() - t0
+    ms_per_step = elapsed * 1e3 / args.steps
+    log(f"[bench] timed {args.steps} steps: {ms_per_step:.3f} ms/step")
+
+    def avg(a, b):
+        return sum(e[a].elapsed_time(e[b]) for e in events) / len(events)
+
+    fwd_ms, pre_ms, dkdv_ms, dq_ms = avg(0, 1), avg(1, 2), avg(2, 3), avg(3, 4)
+    fwd_f, bwd_f = w.fwd_flops(), w.bwd_flops()
+    value = (fwd_f + bwd_f) / (ms_per_step * 1e-3) / 1e12
+
+    ok = all(bool(torch.isfinite(t).all()) for t in (o, lse, dq, dk, dv))
+    if not ok:
+        raise SystemExit("non-finite output")
+
+    # Algorithmic FLOPs per launch: the forward's 2 products; the backward's 5 counted products split
+    # as dK/dV kernel = S, dP, dV, dK (4 of 5) and dQ kernel = dQ (1 of 5) — the dQ kernel's two
+    # recomputed products (S, dP) are extra work, not counted.
+    kernels = {
+        "fwd_bf16_kernel": {"ms": fwd_ms, "flops": fwd_f, "src": "fa_fwd.hip"},
+        "bwd_dkdv_kernel": {"ms": dkdv_ms, "flops": bwd_f * 4 / 5, "src": "fa_bwd.hip"},
+        "bwd_dq_kernel": {"ms": dq_ms, "flops": bwd_f * 1 / 5, "src": "fa_bwd.hip"},
+        "bwd_pre_kernel": {"ms": pre_ms, "src": "fa_bwd.hip"},
+    }
+    for kk in kernels.values():
+        if "flops" in kk:
+            kk["tflops"] = kk["flops"] / (kk["ms"] * 1e-3) / 1e12
+    dom = max(("fwd_bf16_kernel", "bwd_dkdv_kernel", "bwd_dq_kernel"),
+              key=lambda n: kernels[n]["ms"])
+    dom_k = kernels[dom]
+    roofline = {
+        "kernel": dom,
+        "bound": "mfma",
+        "achieved": dom_k["tflops"],
+        "peak": BF16_PEAK_TFLOPS,
+        "unit": "TFLOP/s",
+        "frac": dom_k["tflops"] / BF16_PEAK_TFLOPS,
+        "traffic": measured_traffic(dom, dom_k["src"]),
+        "launch_ms": dom_k["ms"],
+    }
+
+    cpu = None
+    if args.cpu_budget > 0:
+        log(f"[bench] timing the CPU oracle for ~{args.cpu_budget:.0f} s")
+        cpu = cpu_baseline(w, inp, args.cpu_budget)
+        log(f"[bench] oracle: {cpu['value']:.4f} TFLOP/s on {cpu['cores']} threads")
+
+    out = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": B, "H": H, "N": N, "d": d, "causal": w.causal,
+                   "softmax_scale": scale, "flops_per_step": fwd_f + bwd_f},
+        "mfma_peak_frac": value / BF16_PEAK_TFLOPS,
+        "phases_ms": {"fwd": fwd_ms, "bwd_preprocess": pre_ms, "bwd_dkdv": dkdv_ms,
+                      "bwd_dq": dq_ms},
+        "fwd_tflops": fwd_f / (fwd_ms * 1e-3) / 1e12,
+        "bwd_tflops": bwd_f / ((pre_ms + dkdv_ms + dq_ms) * 1e-3) / 1e12,
+        "kernels": {n: {k2: v2 for k2, v2 in kk.items() if k2 != "src"} for n, kk in kernels.items()},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

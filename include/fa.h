@@ -74,9 +74,8 @@ fa_status fa_fwd_fp8(const void* q8, const void* k8, const void* v8,
                      int B, int H, int N, int d, int causal, float softmax_scale, hipStream_t stream);
 
 /*
- * Bytes of device workspace fa_bwd needs for a shape: an fp32 [B,H,N,d] accumulator for dQ plus an
- * fp32 [B,H,N] array for D_i = dO_i · O_i, each rounded up to 256 bytes.  Returns 0 for an
- * unsupported shape.
+ * Bytes of device workspace fa_bwd needs for a shape: an fp32 [B,H,N] array for D_i = dO_i · O_i,
+ * rounded up to 256 bytes.  Returns 0 for an unsupported shape.
  */
 size_t fa_bwd_workspace_bytes(int B, int H, int N, int d);
 
@@ -90,11 +89,30 @@ size_t fa_bwd_workspace_bytes(int B, int H, int N, int d);
  *   workspace         device scratch of at least fa_bwd_workspace_bytes(B,H,N,d) bytes, 256-byte
  *                     aligned, owned by the caller; its contents on entry do not matter and on return
  *                     are unspecified.  It must not be shared by calls in flight at the same time.
- * The low bits of dq may differ from run to run (dQ is summed with atomic adds in unspecified order).
+ * The result is deterministic: no atomics, fixed summation order.
  */
 fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
                  const void* dout, void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
                  int B, int H, int N, int d, int causal, float softmax_scale, hipStream_t stream);
+
+/*
+ * The backward pass as its three phases, for callers that schedule or time them separately.
+ * fa_bwd enqueues exactly these three calls in this order; arguments mean what they mean there and
+ * are checked the same way.  The last two both depend only on the first.
+ *   fa_bwd_preprocess  D_i = dO_i · O_i (fp32) into the workspace.
+ *   fa_bwd_dkdv        recomputes S and P per key tile (key/value-stationary) and writes dK and dV.
+ *   fa_bwd_dq          recomputes S, P and dP per query tile (query-stationary) and writes dQ.
+ */
+fa_status fa_bwd_preprocess(const void* o, const void* dout, void* workspace, size_t workspace_bytes,
+                            int B, int H, int N, int d, hipStream_t stream);
+fa_status fa_bwd_dkdv(const void* q, const void* k, const void* v, const float* lse,
+                      const void* dout, void* dk, void* dv, const void* workspace,
+                      size_t workspace_bytes, int B, int H, int N, int d, int causal,
+                      float softmax_scale, hipStream_t stream);
+fa_status fa_bwd_dq(const void* q, const void* k, const void* v, const float* lse,
+                    const void* dout, void* dq, const void* workspace, size_t workspace_bytes,
+                    int B, int H, int N, int d, int causal, float softmax_scale,
+                    hipStream_t stream);
 
 /* A static, human-readable name for a status code (never NULL). */
 const char* fa_status_str(fa_status status);

@@ -10,6 +10,7 @@ Entry points (same names as the C ABI, without the ``fa_`` prefix):
   fwd_fp8(q8, k8, v8, q_descale, k_descale, v_descale, causal, scale=None) -> (o, lse)
   bwd(q, k, v, o, lse, dout, causal, scale=None, workspace=None) -> (dq, dk, dv)
   bwd_workspace_bytes(B, H, N, d) -> int
+  bwd_preprocess / bwd_dkdv / bwd_dq — the three phases fa_bwd runs, for timing them apart
   status_str(code) -> str
 """
 
@@ -19,8 +20,8 @@ import os
 
 import torch
 
-__all__ = ["fwd", "fwd_fp8", "bwd", "bwd_workspace_bytes", "status_str", "FaError", "library",
-           "LIB_PATH"]
+__all__ = ["fwd", "fwd_fp8", "bwd", "bwd_workspace_bytes", "bwd_preprocess", "bwd_dkdv",
+           "bwd_dq", "status_str", "FaError", "library", "LIB_PATH"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
 
@@ -56,6 +57,12 @@ def library():
         lib.fa_bwd_workspace_bytes.restype = sz
         lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, f, vp]
         lib.fa_bwd.restype = i
+        lib.fa_bwd_preprocess.argtypes = [vp, vp, vp, sz, i, i, i, i, vp]
+        lib.fa_bwd_preprocess.restype = i
+        lib.fa_bwd_dkdv.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, f, vp]
+        lib.fa_bwd_dkdv.restype = i
+        lib.fa_bwd_dq.argtypes = [vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, f, vp]
+        lib.fa_bwd_dq.restype = i
         lib.fa_status_str.argtypes = [i]
         lib.fa_status_str.restype = ctypes.c_char_p
         _lib = lib
@@ -161,3 +168,47 @@ def bwd(q, k, v, o, lse, dout, causal, scale=None, workspace=None):
                                 int(bool(causal)), _scale(scale, d), _stream(q.device))
     _check("fa_bwd", code)
     return dq, dk, dv
+
+
+def bwd_preprocess(o, dout, workspace):
+    """Phase 1 of the backward: D = rowsum(dO ∘ O) into ``workspace``."""
+    _require(o, "o", torch.bfloat16)
+    _require(dout, "dout", torch.bfloat16, o.shape)
+    _require(workspace, "workspace", torch.uint8)
+    B, H, N, d = o.shape
+    with torch.cuda.device(o.device):
+        code = library().fa_bwd_preprocess(o.data_ptr(), dout.data_ptr(), workspace.data_ptr(),
+                                           workspace.numel(), B, H, N, d, _stream(o.device))
+    _check("fa_bwd_preprocess", code)
+
+
+def _bwd_inputs(q, k, v, lse, dout, workspace, outs):
+    _require(q, "q", torch.bfloat16)
+    for t, name in ((k, "k"), (v, "v"), (dout, "dout"), *outs):
+        _require(t, name, torch.bfloat16, q.shape)
+    B, H, N, d = q.shape
+    _require(lse, "lse", torch.float32, (B, H, N))
+    _require(workspace, "workspace", torch.uint8)
+    return B, H, N, d
+
+
+def bwd_dkdv(q, k, v, lse, dout, dk, dv, workspace, causal, scale=None):
+    """Phase 2 of the backward: writes dk and dv (needs bwd_preprocess on the same workspace)."""
+    B, H, N, d = _bwd_inputs(q, k, v, lse, dout, workspace, ((dk, "dk"), (dv, "dv")))
+    with torch.cuda.device(q.device):
+        code = library().fa_bwd_dkdv(q.data_ptr(), k.data_ptr(), v.data_ptr(), lse.data_ptr(),
+                                     dout.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                                     workspace.data_ptr(), workspace.numel(), B, H, N, d,
+                                     int(bool(causal)), _scale(scale, d), _stream(q.device))
+    _check("fa_bwd_dkdv", code)
+
+
+def bwd_dq(q, k, v, lse, dout, dq, workspace, causal, scale=None):
+    """Phase 3 of the backward: writes dq (needs bwd_preprocess on the same workspace)."""
+    B, H, N, d = _bwd_inputs(q, k, v, lse, dout, workspace, ((dq, "dq"),))
+    with torch.cuda.device(q.device):
+        code = library().fa_bwd_dq(q.data_ptr(), k.data_ptr(), v.data_ptr(), lse.data_ptr(),
+                                   dout.data_ptr(), dq.data_ptr(), workspace.data_ptr(),
+                                   workspace.numel(), B, H, N, d, int(bool(causal)),
+                                   _scale(scale, d), _stream(q.device))
+    _check("fa_bwd_dq", code)

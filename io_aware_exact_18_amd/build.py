@@ -46,7 +46,8 @@ def _compile(src, extra):
     cmd = [hipcc(), *COMMON_FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
-        raise RuntimeError(f"hipcc failed for {src}:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+        err = "\n".join(l for l in r.stderr.splitlines() if "error" in l)[:4000]
+        raise RuntimeError(f"hipcc failed for {src}:\n{' '.join(cmd)}\n{err or r.stderr[-4000:]}")
     return obj, r.stderr
 
 

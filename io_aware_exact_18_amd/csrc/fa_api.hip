@@ -75,7 +75,89 @@ fa_status fa_fwd_fp8(const void* q8, const void* k8, const void* v8, float q_des
 
 size_t fa_bwd_workspace_bytes(int B, int H, int N, int d) {
   if (check_shape(B, H, N, d, 2) != FA_OK) return 0;
-  return fa::bwd_dq_acc_bytes(B, H, N, d) + fa::bwd_delta_bytes(B, H, N);
+  return fa::bwd_delta_bytes(B, H, N);
+}
+
+}  // extern "C"
+
+namespace {
+
+// Shape, workspace and alignment checks shared by the backward entry points.  `ptrs` are the tensor
+// pointers the call uses (NULL ones were rejected before).
+fa_status check_bwd(const void* const* ptrs, int n_ptrs, const void* workspace, size_t ws_bytes,
+                    int B, int H, int N, int d, fa::BwdArgs* a) {
+  fa_status st = check_shape(B, H, N, d, 2);
+  if (st != FA_OK) return st;
+  if (!workspace || ws_bytes < fa_bwd_workspace_bytes(B, H, N, d)) return FA_ERR_WORKSPACE;
+  for (int i = 0; i < n_ptrs; ++i)
+    if (!aligned(ptrs[i], 16)) return FA_ERR_ALIGN;
+  if (!aligned(workspace, 256)) return FA_ERR_ALIGN;
+  a->delta = (float*)workspace;
+  a->B = B;
+  a->H = H;
+  a->N = N;
+  a->d = d;
+  return FA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+fa_status fa_bwd_preprocess(const void* o, const void* dout, void* workspace,
+                            size_t workspace_bytes, int B, int H, int N, int d,
+                            hipStream_t stream) {
+  if (!o || !dout) return FA_ERR_NULL;
+  fa::BwdArgs a{};
+  const void* ptrs[] = {o, dout};
+  fa_status st = check_bwd(ptrs, 2, workspace, workspace_bytes, B, H, N, d, &a);
+  if (st != FA_OK) return st;
+  a.o = o;
+  a.dout = dout;
+  return fa::launch_bwd_pre(a, stream) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+fa_status fa_bwd_dkdv(const void* q, const void* k, const void* v, const float* lse,
+                      const void* dout, void* dk, void* dv, const void* workspace,
+                      size_t workspace_bytes, int B, int H, int N, int d, int causal,
+                      float softmax_scale, hipStream_t stream) {
+  if (!q || !k || !v || !lse || !dout || !dk || !dv) return FA_ERR_NULL;
+  fa::BwdArgs a{};
+  const void* ptrs[] = {q, k, v, lse, dout, dk, dv};
+  fa_status st = check_bwd(ptrs, 7, workspace, workspace_bytes, B, H, N, d, &a);
+  if (st != FA_OK) return st;
+  if (!good_scale(softmax_scale)) return FA_ERR_UNSUPPORTED;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.lse = lse;
+  a.dout = dout;
+  a.dk = dk;
+  a.dv = dv;
+  a.causal = causal ? 1 : 0;
+  a.scale = softmax_scale;
+  return fa::launch_bwd_dkdv(a, stream) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+fa_status fa_bwd_dq(const void* q, const void* k, const void* v, const float* lse,
+                    const void* dout, void* dq, const void* workspace, size_t workspace_bytes,
+                    int B, int H, int N, int d, int causal, float softmax_scale,
+                    hipStream_t stream) {
+  if (!q || !k || !v || !lse || !dout || !dq) return FA_ERR_NULL;
+  fa::BwdArgs a{};
+  const void* ptrs[] = {q, k, v, lse, dout, dq};
+  fa_status st = check_bwd(ptrs, 6, workspace, workspace_bytes, B, H, N, d, &a);
+  if (st != FA_OK) return st;
+  if (!good_scale(softmax_scale)) return FA_ERR_UNSUPPORTED;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.lse = lse;
+  a.dout = dout;
+  a.dq = dq;
+  a.causal = causal ? 1 : 0;
+  a.scale = softmax_scale;
+  return fa::launch_bwd_dq(a, stream) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
 fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
@@ -83,19 +165,26 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
                  size_t workspace_bytes, int B, int H, int N, int d, int causal,
                  float softmax_scale, hipStream_t stream) {
   if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return FA_ERR_NULL;
-  fa_status st = check_shape(B, H, N, d, 2);
+  fa::BwdArgs a{};
+  const void* ptrs[] = {q, k, v, o, lse, dout, dq, dk, dv};
+  fa_status st = check_bwd(ptrs, 9, workspace, workspace_bytes, B, H, N, d, &a);
   if (st != FA_OK) return st;
   if (!good_scale(softmax_scale)) return FA_ERR_UNSUPPORTED;
-  if (!workspace || workspace_bytes < fa_bwd_workspace_bytes(B, H, N, d)) return FA_ERR_WORKSPACE;
-  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
-      !aligned(lse, 16) || !aligned(dout, 16) || !aligned(dq, 16) || !aligned(dk, 16) ||
-      !aligned(dv, 16) || !aligned(workspace, 256))
-    return FA_ERR_ALIGN;
-  float* dq_acc = (float*)workspace;
-  float* delta = (float*)((char*)workspace + fa::bwd_dq_acc_bytes(B, H, N, d));
-  fa::BwdArgs a{q, k, v, o, lse, dout, dq, dk, dv, dq_acc, delta,
-                B, H, N, d, causal ? 1 : 0, softmax_scale};
-  return fa::launch_bwd_bf16(a, stream) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.dout = dout;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.causal = causal ? 1 : 0;
+  a.scale = softmax_scale;
+  if (fa::launch_bwd_pre(a, stream) != hipSuccess) return FA_ERR_LAUNCH;
+  if (fa::launch_bwd_dkdv(a, stream) != hipSuccess) return FA_ERR_LAUNCH;
+  if (fa::launch_bwd_dq(a, stream) != hipSuccess) return FA_ERR_LAUNCH;
+  return FA_OK;
 }
 
 }  // extern "C"

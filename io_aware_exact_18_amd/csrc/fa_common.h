@@ -75,6 +75,14 @@ __device__ inline float halves_sum(float x) {
 
 __device__ inline float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Wait for every outstanding vector-memory load of this wave.  Used once after loads made before a
+// loop whose body consumes them: otherwise the wait the compiler inserts inside the loop is counted
+// against the loop's own prefetch loads and exposes their latency on every iteration.
+__device__ inline void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
+
+// True when `pred` holds on every active lane of the wave (a wave-uniform answer).
+__device__ inline bool wave_all(bool pred) { return __builtin_amdgcn_ballot_w64(!pred) == 0; }
+
 // Round two floats to bf16 (round-to-nearest-even) and pack them, first in the low half.
 __device__ inline uint32_t pack_bf16x2(float lo, float hi) {
   typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
@@ -94,6 +102,35 @@ __device__ inline int swz_f(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
 template <int D>
 __device__ inline int tile_off(int row, int col) {
   return row * D + ((((col >> 3) ^ swz_f(row)) << 3) | (col & 7));
+}
+
+// Asynchronous copy of a [ROWS][D] bf16 tile (rows row0 .. row0+ROWS-1 of a [*, D] matrix behind the
+// buffer resource `r`) into LDS in the tile_off<D> layout, by NT threads, without passing through
+// registers (buffer_load_dwordx4 ... lds: lane i of a wave writes LDS bytes [16 i, 16 i + 16) after the
+// wave-uniform base).  Rows past the buffer's end read as zeros.  Completion: wait_vmem_all().
+template <int D, int ROWS, int NT>
+__device__ inline void tile_to_lds(__amdgpu_buffer_rsrc_t r, int row0, bf16* lds, int tid) {
+  constexpr int CPR = D / 8;  // 16-byte chunks per row
+  constexpr int CHUNKS = ROWS * CPR;
+  static_assert(CHUNKS % NT == 0, "tile must split evenly over the threads");
+  const int wave = tid >> 6, lane = tid & 63;
+#pragma unroll
+  for (int i = 0; i < CHUNKS / NT; ++i) {
+    const int blk = i * (NT / 64) + wave;  // 1 KB block of the tile written by this wave
+    const int slot = blk * 64 + lane;      // physical 16-byte slot
+    const int row = slot / CPR, pc = slot % CPR;
+    const int c = pc ^ swz_f(row);         // logical chunk held by physical chunk pc
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        r, (__attribute__((address_space(3))) void*)(lds + blk * 512), 16,
+        (uint32_t)((row0 + row) * D + 8 * c) * 2u, 0, 0, 0);
+  }
+}
+
+// Asynchronous copy of 64 consecutive fp32 values (elements e0 .. e0+63 behind `r`) into LDS by one
+// wave; values past the buffer's end read as zeros.
+__device__ inline void vec64_to_lds(__amdgpu_buffer_rsrc_t r, int e0, float* lds, int lane) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 4,
+                                           (uint32_t)(e0 + lane) * 4u, 0, 0, 0);
 }
 
 // blockIdx → logical work item such that consecutive logical items land on the same XCD: logical

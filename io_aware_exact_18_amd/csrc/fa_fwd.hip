@@ -7,8 +7,8 @@
 //
 // Work split (gfx950, wave64):
 //   * 4 waves per workgroup, 32 queries per wave: B_r = 128.  Key/value tiles of B_c = 64 rows are
-//     staged in LDS (double-buffered, one barrier per tile, XOR-swizzled rows) and shared by the 4
-//     waves.
+//     copied straight from memory into LDS (buffer_load ... lds; double-buffered, one barrier per
+//     tile, XOR-swizzled rows) and shared by the 4 waves.
 //   * Each wave computes the transposed score tile Sᵀ = K Qᵀ on the 32×32×16 bf16 matrix core, so
 //     every lane owns one query column: the row maximum and row sum of the softmax are in-lane
 //     reductions plus one exchange between the two half-waves (v_permlane32_swap).
@@ -42,7 +42,6 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     bf16* __restrict__ O, float* __restrict__ LSE, int N, int nqt, float scale_log2, int remap) {
   constexpr int KSTEPS = D / 16;                 // k-steps of the Sᵀ product
   constexpr int DB = D / 32;                     // 32-row blocks of Oᵀ
-  constexpr int CH = kBC * D / 8 / kThreads;     // 16-byte chunks per thread per K (or V) tile
   __shared__ FwdSmem<D> sm;
 
   const int tid = threadIdx.x;
@@ -75,29 +74,9 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
   const int kv_end = CAUSAL ? min(N, q0 + kBR) : N;
   const int ntiles = (kv_end + kBC - 1) / kBC;
 
-  u32x4 kreg[CH], vreg[CH];
-  auto load_tile = [&](int t) {
-#pragma unroll
-    for (int i = 0; i < CH; ++i) {
-      const int c = tid + kThreads * i;
-      const int row = c / (D / 8), col = (c % (D / 8)) * 8;
-      const uint32_t off = (uint32_t)((t * kBC + row) * D + col) * 2u;
-      kreg[i] = buf_load16(rk, off);
-      vreg[i] = buf_load16(rv, off);
-    }
-  };
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < CH; ++i) {
-      const int c = tid + kThreads * i;
-      const int row = c / (D / 8), col = (c % (D / 8)) * 8;
-      *(u32x4*)&sm.k[buf][tile_off<D>(row, col)] = kreg[i];
-      *(u32x4*)&sm.v[buf][tile_off<D>(row, col)] = vreg[i];
-    }
-  };
-
-  load_tile(0);
-  store_tile(0);
+  tile_to_lds<D, kBC, kThreads>(rk, 0, sm.k[0], tid);
+  tile_to_lds<D, kBC, kThreads>(rv, 0, sm.v[0], tid);
+  wait_vmem_all();
   __syncthreads();
 
   float m = -INFINITY;  // running max of the base-2 scaled scores
@@ -117,12 +96,15 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
   for (int j = 0; j < ntiles; ++j) {
     const int buf = j & 1;
     const bool more = j + 1 < ntiles;
-    if (more) load_tile(j + 1);
+    if (more) {  // next tile streams into the other buffer while this one is used
+      tile_to_lds<D, kBC, kThreads>(rk, (j + 1) * kBC, sm.k[buf ^ 1], tid);
+      tile_to_lds<D, kBC, kThreads>(rv, (j + 1) * kBC, sm.v[buf ^ 1], tid);
+    }
     const int kv0 = j * kBC;
 
     if (!(CAUSAL && kv0 > qw + 31)) {  // tile fully masked for this wave: skip the math
-      const bf16* ks = sm.k[buf];
-      const bf16* vs = sm.v[buf];
+      const bf16* klds = sm.k[buf];
+      const bf16* vlds = sm.v[buf];
       f32x16 sacc[2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
@@ -130,7 +112,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
         for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
 #pragma unroll
         for (int s = 0; s < KSTEPS; ++s) {
-          const bf16x8 kf = *(const bf16x8*)&ks[tile_off<D>(kb * 32 + lc, 16 * s + 8 * g)];
+          const bf16x8 kf = *(const bf16x8*)&klds[tile_off<D>(kb * 32 + lc, 16 * s + 8 * g)];
           sacc[kb] = mfma_32x32x16(kf, qf[s], sacc[kb]);
         }
       }
@@ -154,21 +136,25 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
       const float m_new = fmaxf(m, mx * scale_log2);
       const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
       const float alpha = exp2_fast(m - m_use);
-      float rs = 0.f;
+      float rs[4] = {0.f, 0.f, 0.f, 0.f};  // four partial sums: shorter dependency chains
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const float p = exp2_fast(fmaf(sacc[kb][r], scale_log2, -m_use));
           sacc[kb][r] = p;
-          rs += p;
+          rs[r & 3] += p;
         }
-      l = fmaf(l, alpha, rs);
+      l = fmaf(l, alpha, (rs[0] + rs[1]) + (rs[2] + rs[3]));
+      // Rescale the output accumulator only when some row's maximum moved (alpha != 1 somewhere in
+      // the wave); once the maxima settle, most tiles skip these multiplies.
+      if (!wave_all(m_new == m)) {
+#pragma unroll
+        for (int b = 0; b < DB; ++b)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[b][r] *= alpha;
+      }
       m = m_new;
-#pragma unroll
-      for (int b = 0; b < DB; ++b)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[b][r] *= alpha;
 
       // Pᵀ operand for k-step ks (16 keys): slots e = registers 8(ks%2) + e of key block ks/2, i.e.
       // keys 16ks + 8(e/4) + 4g + (e%4) — the order the transposed V reads below produce.
@@ -184,14 +170,14 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
         for (int ks = 0; ks < 4; ++ks) {
           const int key = 16 * ks + 4 * g + tr_a;
           const int col = 32 * b + tr_n + 4 * tr_b;
-          const u32x2 lo = lds_read_tr16(&vs[tile_off<D>(key, col)]);
-          const u32x2 hi = lds_read_tr16(&vs[tile_off<D>(key + 8, col)]);
+          const u32x2 lo = lds_read_tr16(&vlds[tile_off<D>(key, col)]);
+          const u32x2 hi = lds_read_tr16(&vlds[tile_off<D>(key + 8, col)]);
           const u32x4 vv = {lo[0], lo[1], hi[0], hi[1]};
           oacc[b] = mfma_32x32x16(__builtin_bit_cast(bf16x8, vv), pf[ks], oacc[b]);
         }
       }
     }
-    if (more) store_tile(buf ^ 1);
+    wait_vmem_all();
     __syncthreads();
   }
 

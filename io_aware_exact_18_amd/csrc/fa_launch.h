@@ -37,21 +37,19 @@ struct BwdArgs {
   void* dq;
   void* dk;
   void* dv;
-  float* dq_acc;  // fp32 [B,H,N,d] workspace
-  float* delta;   // fp32 [B,H,N] workspace: D_i = dO_i · O_i
+  float* delta;  // fp32 [B,H,N] workspace: D_i = dO_i · O_i
   int B, H, N, d, causal;
   float scale;
 };
 
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_fwd_fp8(const Fp8FwdArgs& a, hipStream_t stream);
-hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t stream);
+hipError_t launch_bwd_pre(const BwdArgs& a, hipStream_t stream);
+hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t stream);
+hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t stream);
 
-// Workspace split used by launch_bwd_bf16: dq_acc first, then delta, each rounded up to 256 bytes.
+// Backward workspace: the fp32 [B,H,N] array D, rounded up to 256 bytes.
 inline size_t round_up_256(size_t x) { return (x + 255u) & ~(size_t)255u; }
-inline size_t bwd_dq_acc_bytes(int B, int H, int N, int d) {
-  return round_up_256((size_t)B * H * N * d * sizeof(float));
-}
 inline size_t bwd_delta_bytes(int B, int H, int N) {
   return round_up_256((size_t)B * H * N * sizeof(float));
 }

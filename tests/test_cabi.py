@@ -27,6 +27,9 @@ def lib():
     lib.fa_bwd_workspace_bytes.argtypes = [i, i, i, i]
     lib.fa_bwd_workspace_bytes.restype = sz
     lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, f, vp]
+    lib.fa_bwd_preprocess.argtypes = [vp, vp, vp, sz, i, i, i, i, vp]
+    lib.fa_bwd_dkdv.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, f, vp]
+    lib.fa_bwd_dq.argtypes = [vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, f, vp]
     lib.fa_status_str.argtypes = [i]
     lib.fa_status_str.restype = ctypes.c_char_p
     return lib
@@ -35,7 +38,8 @@ def lib():
 def test_exports_match_header(lib):
     text = open(HEADER).read()
     declared = set(re.findall(r"^\s*(?:fa_status|size_t|const char\*)\s+(fa_\w+)\s*\(", text, re.M))
-    assert declared == {"fa_fwd", "fa_fwd_fp8", "fa_bwd_workspace_bytes", "fa_bwd", "fa_status_str"}
+    assert declared == {"fa_fwd", "fa_fwd_fp8", "fa_bwd_workspace_bytes", "fa_bwd", "fa_status_str",
+                        "fa_bwd_preprocess", "fa_bwd_dkdv", "fa_bwd_dq"}
     for name in declared:
         assert hasattr(lib, name), name
 
@@ -86,7 +90,7 @@ def test_workspace_bytes(lib):
     def up(x):
         return (x + 255) // 256 * 256
     for B, H, N, d in ((1, 1, 1, 64), (8, 16, 2048, 64), (4, 32, 4096, 128), (1, 3, 17, 128)):
-        assert lib.fa_bwd_workspace_bytes(B, H, N, d) == up(B * H * N * d * 4) + up(B * H * N * 4)
+        assert lib.fa_bwd_workspace_bytes(B, H, N, d) == up(B * H * N * 4)
     assert lib.fa_bwd_workspace_bytes(1, 1, 64, 96) == 0
     assert lib.fa_bwd_workspace_bytes(0, 1, 64, 64) == 0
 
@@ -104,9 +108,24 @@ def test_bwd_rejections(lib):
     assert bwd(lib, d=80) == UNSUP
     assert bwd(lib, scale=math.inf) == UNSUP
     assert bwd(lib, ws=None) == WORKSPACE
-    assert bwd(lib, ws_bytes=1024) == WORKSPACE
+    assert bwd(lib, ws_bytes=64) == WORKSPACE
     assert bwd(lib, ws=P + 16) == ALIGN       # workspace needs 256-byte alignment
     assert bwd(lib, dq=MIS) == ALIGN
+
+
+def test_bwd_phase_rejections(lib):
+    ws = lib.fa_bwd_workspace_bytes(1, 1, 64, 64)
+    assert lib.fa_bwd_preprocess(None, P, P, ws, 1, 1, 64, 64, None) == NULL
+    assert lib.fa_bwd_preprocess(P, P, P, ws - 4, 1, 1, 64, 64, None) == WORKSPACE
+    assert lib.fa_bwd_preprocess(P, MIS, P, ws, 1, 1, 64, 64, None) == ALIGN
+    assert lib.fa_bwd_dkdv(P, P, P, P, P, P, None, P, ws, 1, 1, 64, 64, 0, 0.1, None) == NULL
+    assert lib.fa_bwd_dkdv(P, P, P, P, P, P, P, P, ws, 1, 1, 64, 48, 0, 0.1, None) == UNSUP
+    assert lib.fa_bwd_dkdv(P, P, P, P, P, P, P, P, ws, 1, 1, 64, 64, 0, 0.0, None) == UNSUP
+    assert lib.fa_bwd_dkdv(P, P, P, P, P, P, P, None, ws, 1, 1, 64, 64, 0, 0.1, None) == WORKSPACE
+    assert lib.fa_bwd_dq(P, P, P, P, P, None, P, ws, 1, 1, 64, 64, 1, 0.1, None) == NULL
+    assert lib.fa_bwd_dq(P, P, P, P, P, P, P + 128, ws, 1, 1, 64, 64, 1, 0.1, None) == ALIGN
+    assert lib.fa_bwd_dq(P, P, P, P, P, P, P, ws, 1, 0, 64, 64, 1, 0.1, None) == SHAPE
+    assert lib.fa_bwd_dq(P, P, P, P, MIS, P, P, ws, 1, 1, 64, 64, 1, 0.1, None) == ALIGN
 
 
 def test_binding_fails_loudly_without_tensors_on_gpu():

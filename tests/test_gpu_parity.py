@@ -304,3 +304,26 @@ def test_workload_long_full():
     _check_bwd_heads(inp["q"], inp["k"], inp["v"], inp["do"], dq.cpu(), dk.cpu(), dv.cpu(),
                      w.causal, w.scale, [B * H - 1])
     _check_bwd_sums(inp["do"], dk, dv)
+
+
+def test_bwd_phases_equal_fused_call():
+    """fa_bwd_preprocess + fa_bwd_dkdv + fa_bwd_dq give bitwise what fa_bwd gives, and fa_bwd is
+    deterministic from run to run."""
+    B, H, N, d = 2, 2, 333, 128
+    g = torch.Generator().manual_seed(15)
+    q, k, v, do = (torch.randn(B, H, N, d, generator=g).to(torch.bfloat16).cuda() for _ in range(4))
+    scale = 1.0 / math.sqrt(d)
+    for causal in (False, True):
+        o, lse = fa().fwd(q, k, v, causal, scale)
+        dq, dk, dv = fa().bwd(q, k, v, o, lse, do, causal, scale)
+        again = fa().bwd(q, k, v, o, lse, do, causal, scale)
+        ws = torch.empty(fa().bwd_workspace_bytes(B, H, N, d), dtype=torch.uint8, device="cuda")
+        dq2, dk2, dv2 = (torch.empty_like(q) for _ in range(3))
+        fa().bwd_preprocess(o, do, ws)
+        fa().bwd_dkdv(q, k, v, lse, do, dk2, dv2, ws, causal, scale)
+        fa().bwd_dq(q, k, v, lse, do, dq2, ws, causal, scale)
+        torch.cuda.synchronize()
+        for a, b in zip((dq, dk, dv), (dq2, dk2, dv2)):
+            assert torch.equal(a, b)
+        for a, b in zip((dq, dk, dv), again):
+            assert torch.equal(a, b)
