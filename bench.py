@@ -98,6 +98,9 @@ def main():
                     help="bf16 forward+backward workload (default: the throughput workload)")
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle work for the cpu_baseline leg (0 skips it)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="instead of the bench, run a plain device copy of MIB MiB `--steps` times "
+                         "(the reference kernel for scaling HBM byte counters)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -112,6 +115,15 @@ def main():
     import workloads
 
     assert torch.cuda.is_available(), "bench.py needs a ROCm device"
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "copies": args.steps}))
+        return
     w = workloads.WORKLOADS[args.workload]
     if w.fp8 or not w.backward:
         raise SystemExit("choose a bf16 forward+backward workload")

@@ -11,9 +11,9 @@
 // Three launches on the caller's stream, none with atomics:
 //   1. bwd_pre: D_i = dO_i · O_i in fp32 (workspace).
 //   2. bwd_dkdv: key/value-stationary.  One workgroup per 128 keys (4 waves × 32 keys).  Each wave
-//      keeps its K and V rows as matrix-core operands and its dKᵀ, dVᵀ accumulators in registers and
-//      walks the 32-query tiles the causal mask allows, staged in LDS by direct buffer→LDS copies
-//      (double-buffered, one barrier per tile).  Per tile: S = Q Kᵀ and dP = dO Vᵀ (32×32×16 bf16
+//      keeps its K rows as matrix-core operands and its dKᵀ, dVᵀ accumulators in registers (V rows
+//      stay in LDS) and walks the 32-query tiles the causal mask allows, staged in LDS by direct
+//      buffer→LDS copies (double-buffered, one barrier per tile).  Per tile: S = Q Kᵀ and dP = dO Vᵀ (32×32×16 bf16
 //      matrix cores, Q and dO rows from LDS), P and dS on the vector units, then dVᵀ += dOᵀ P and
 //      dKᵀ += Qᵀ dS with transposed LDS reads supplying dOᵀ and Qᵀ.
 //   3. bwd_dq: query-stationary, the same shape as the forward: one workgroup per 128 queries
@@ -25,6 +25,8 @@
 // adds sustain about 1.3 TB/s, which for the 4096-token causal workload alone would take ~3 ms.
 #include "fa_common.h"
 #include "fa_launch.h"
+
+#include <type_traits>
 
 namespace fa {
 namespace {
@@ -61,14 +63,6 @@ __global__ __launch_bounds__(kThreads) void bwd_pre_kernel(const bf16* __restric
 
 // ---------------------------------------------------------------------------------------------------
 // 2. dK, dV.
-template <int D>
-struct DkdvSmem {
-  bf16 q[2][kBQ * D];     // Q tile (tile_off<D> layout), double-buffered
-  bf16 dout[2][kBQ * D];  // dO tile
-  float lse[2][64];       // LSE of the tile's queries (first 32 used)
-  float delta[2][64];     // D_i of the tile's queries (first 32 used)
-};
-
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
@@ -77,16 +71,24 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(
     int remap) {
   constexpr int KSTEPS = D / 16;
   constexpr int DB = D / 32;
-  __shared__ DkdvSmem<D> sm;
+  // Q and dO tiles (tile_off<D> layout) and the tile's LSE and D values (first 32 of 64 used),
+  // double-buffered; separate LDS objects so reads of one buffer never wait for the LDS-DMA copy
+  // filling the other.
+  __shared__ __attribute__((aligned(1024))) bf16 q0s[kBQ * D];
+  __shared__ __attribute__((aligned(1024))) bf16 q1s[kBQ * D];
+  __shared__ __attribute__((aligned(1024))) bf16 o0s[kBQ * D];
+  __shared__ __attribute__((aligned(1024))) bf16 o1s[kBQ * D];
+  __shared__ __attribute__((aligned(256))) float l0s[64];
+  __shared__ __attribute__((aligned(256))) float l1s[64];
+  __shared__ __attribute__((aligned(256))) float d0s[64];
+  __shared__ __attribute__((aligned(256))) float d1s[64];
+  __shared__ __attribute__((aligned(1024))) bf16 vts[kBKV * D];  // the workgroup's V rows
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int g = lane >> 5;
   const int lc = lane & 31;
-  const int tr_a = (lane & 15) >> 2;
-  const int tr_b = lane & 3;
-  const int tr_n = 16 * ((lane >> 4) & 1);
 
   const uint32_t logical = remap ? xcd_remap(blockIdx.x, gridDim.x) : blockIdx.x;
   const int bh = logical / nkt;
@@ -104,24 +106,25 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(
   const auto rlse = make_rsrc(LSE + (size_t)bh * N, (uint32_t)N * 4u);
   const auto rdel = make_rsrc(Delta + (size_t)bh * N, (uint32_t)N * 4u);
 
-  // Kᵀ and Vᵀ operands (B operands of S = Q Kᵀ and dP = dO Vᵀ): column = this lane's key.
-  bf16x8 kf[KSTEPS], vf[KSTEPS];
+  // Kᵀ operands (B operand of S = Q Kᵀ) in registers: column = this lane's key.  The Vᵀ operand of
+  // dP = dO Vᵀ is read from the LDS copy of the workgroup's V rows each step (registers are the
+  // scarce resource here: dKᵀ and dVᵀ accumulators take 128 of them).
+  bf16x8 kf[KSTEPS];
 #pragma unroll
-  for (int s = 0; s < KSTEPS; ++s) {
-    const uint32_t off = (uint32_t)(kj * D + 16 * s + 8 * g) * 2u;
-    kf[s] = __builtin_bit_cast(bf16x8, buf_load16(rk, off));
-    vf[s] = __builtin_bit_cast(bf16x8, buf_load16(rv, off));
-  }
+  for (int s = 0; s < KSTEPS; ++s)
+    kf[s] = __builtin_bit_cast(bf16x8, buf_load16(rk, (uint32_t)(kj * D + 16 * s + 8 * g) * 2u));
+  tile_to_lds<D, kBKV, kThreads>(rv, k0, vts, tid);
 
+  const FragOffsets<D> fo(lane);
   const int qstart = CAUSAL ? k0 : 0;  // causal: only queries ≥ the tile's first key
   const int nsteps = (N - qstart + kBQ - 1) / kBQ;
 
-  auto stage = [&](int step, int buf) {
+  auto stage = [&](int step, bf16* qd, bf16* od, float* ld, float* dd) {
     const int qb = qstart + step * kBQ;
-    tile_to_lds<D, kBQ, kThreads>(rq, qb, sm.q[buf], tid);
-    tile_to_lds<D, kBQ, kThreads>(rdo, qb, sm.dout[buf], tid);
-    if (wave == 0) vec64_to_lds(rlse, qb, sm.lse[buf], lane);
-    if (wave == 1) vec64_to_lds(rdel, qb, sm.delta[buf], lane);
+    tile_to_lds<D, kBQ, kThreads>(rq, qb, qd, tid);
+    tile_to_lds<D, kBQ, kThreads>(rdo, qb, od, tid);
+    if (wave == 0) vec64_to_lds(rlse, qb, ld, lane);
+    if (wave == 1) vec64_to_lds(rdel, qb, dd, lane);
   };
 
   f32x16 dka[DB], dva[DB];  // dKᵀ, dVᵀ: rows = d (32b + 8(r/4) + 4g + r%4), column = key
@@ -133,19 +136,22 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(
       dva[b][r] = 0.f;
     }
 
-  stage(0, 0);
+  stage(0, q0s, o0s, l0s, d0s);
   wait_vmem_all();
   __syncthreads();
 
-  for (int step = 0; step < nsteps; ++step) {
-    const int buf = step & 1;
-    const bool more = step + 1 < nsteps;
-    if (more) stage(step + 1, buf ^ 1);
+  // One query tile; P (the step's parity) is a compile-time constant so the buffers are fixed
+  // objects.  On entry the tile is in buffer P; buffer P^1 is free and receives the next tile.
+  auto step_fn = [&](auto parity, int step) {
+    constexpr int P = decltype(parity)::value;
+    const char* qs = (const char*)(P ? q1s : q0s);
+    const char* dos = (const char*)(P ? o1s : o0s);
+    const float* lse_s = P ? l1s : l0s;
+    const float* del_s = P ? d1s : d0s;
+    if (step + 1 < nsteps) stage(step + 1, P ? q0s : q1s, P ? o0s : o1s, P ? l0s : l1s, P ? d0s : d1s);
     const int qb = qstart + step * kBQ;
 
     if (!(CAUSAL && kw > qb + kBQ - 1)) {  // every (query, key) pair masked for this wave: skip
-      const bf16* qs = sm.q[buf];
-      const bf16* dos = sm.dout[buf];
       // S = Q Kᵀ and dP = dO Vᵀ for 32 queries × this wave's 32 keys.
       f32x16 sacc, pacc;
 #pragma unroll
@@ -155,17 +161,16 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(
       }
 #pragma unroll
       for (int s = 0; s < KSTEPS; ++s) {
-        const bf16x8 qa = *(const bf16x8*)&qs[tile_off<D>(lc, 16 * s + 8 * g)];
-        const bf16x8 da = *(const bf16x8*)&dos[tile_off<D>(lc, 16 * s + 8 * g)];
-        sacc = mfma_32x32x16(qa, kf[s], sacc);
-        pacc = mfma_32x32x16(da, vf[s], pacc);
+        sacc = mfma_32x32x16(row_frag<D>(qs, fo, 0, s), kf[s], sacc);
+        pacc = mfma_32x32x16(row_frag<D>(dos, fo, 0, s), row_frag<D>((const char*)vts, fo, wave, s),
+                             pacc);
       }
       // Element r: query qb + 8(r/4) + 4g + (r%4), key kj.
       const bool need_mask = (kw + 31 >= N) || (CAUSAL && kw + 31 > qb);
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
-        const f32x4 l4 = *(const f32x4*)&sm.lse[buf][8 * r4 + 4 * g];
-        const f32x4 d4 = *(const f32x4*)&sm.delta[buf][8 * r4 + 4 * g];
+        const f32x4 l4 = *(const f32x4*)&lse_s[8 * r4 + 4 * g];
+        const f32x4 d4 = *(const f32x4*)&del_s[8 * r4 + 4 * g];
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
           const int r = 4 * r4 + t;
@@ -191,21 +196,18 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(
       for (int b = 0; b < DB; ++b) {
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-          const int qrow = 16 * ks + 4 * g + tr_a;
-          const int col = 32 * b + tr_n + 4 * tr_b;
-          const u32x2 dlo = lds_read_tr16(&dos[tile_off<D>(qrow, col)]);
-          const u32x2 dhi = lds_read_tr16(&dos[tile_off<D>(qrow + 8, col)]);
-          const u32x2 qlo = lds_read_tr16(&qs[tile_off<D>(qrow, col)]);
-          const u32x2 qhi = lds_read_tr16(&qs[tile_off<D>(qrow + 8, col)]);
-          const u32x4 dv4 = {dlo[0], dlo[1], dhi[0], dhi[1]};
-          const u32x4 qv4 = {qlo[0], qlo[1], qhi[0], qhi[1]};
-          dva[b] = mfma_32x32x16(__builtin_bit_cast(bf16x8, dv4), pb[ks], dva[b]);
-          dka[b] = mfma_32x32x16(__builtin_bit_cast(bf16x8, qv4), dsb[ks], dka[b]);
+          dva[b] = mfma_32x32x16(tr_frag<D>(dos, fo, ks, b), pb[ks], dva[b]);
+          dka[b] = mfma_32x32x16(tr_frag<D>(qs, fo, ks, b), dsb[ks], dka[b]);
         }
       }
     }
     wait_vmem_all();
     __syncthreads();
+  };
+
+  for (int step = 0; step < nsteps; step += 2) {
+    step_fn(std::integral_constant<int, 0>{}, step);
+    if (step + 1 < nsteps) step_fn(std::integral_constant<int, 1>{}, step + 1);
   }
 
   // Epilogue: dK = scale · (dKᵀ)ᵀ, dV = (dVᵀ)ᵀ; this lane owns key kj, d rows 32b + 8(r/4) + 4g + (0..3).
@@ -229,12 +231,6 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(
 
 // ---------------------------------------------------------------------------------------------------
 // 3. dQ.
-template <int D>
-struct DqSmem {
-  bf16 k[2][kBC * D];  // tile_off<D> layout, double-buffered
-  bf16 v[2][kBC * D];
-};
-
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
@@ -242,16 +238,18 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
     bf16* __restrict__ dQ, int N, int nqt, float scale, float scale_log2, int remap) {
   constexpr int KSTEPS = D / 16;
   constexpr int DB = D / 32;
-  __shared__ DqSmem<D> sm;
+  // K and V tiles (tile_off<D> layout), double-buffered, as separate LDS objects (see the dK/dV
+  // kernel).
+  __shared__ __attribute__((aligned(1024))) bf16 k0s[kBC * D];
+  __shared__ __attribute__((aligned(1024))) bf16 k1s[kBC * D];
+  __shared__ __attribute__((aligned(1024))) bf16 v0s[kBC * D];
+  __shared__ __attribute__((aligned(1024))) bf16 v1s[kBC * D];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int g = lane >> 5;
   const int lc = lane & 31;
-  const int tr_a = (lane & 15) >> 2;
-  const int tr_b = lane & 3;
-  const int tr_n = 16 * ((lane >> 4) & 1);
 
   const uint32_t logical = remap ? xcd_remap(blockIdx.x, gridDim.x) : blockIdx.x;
   const int bh = logical / nqt;
@@ -283,6 +281,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
 
   const int kv_end = CAUSAL ? min(N, q0 + kBR) : N;
   const int ntiles = (kv_end + kBC - 1) / kBC;
+  const FragOffsets<D> fo(lane);
 
   f32x16 qacc[DB];  // dQᵀ: rows d = 32b + 8(r/4) + 4g + r%4, column = this lane's query
 #pragma unroll
@@ -290,22 +289,22 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
 #pragma unroll
     for (int r = 0; r < 16; ++r) qacc[b][r] = 0.f;
 
-  tile_to_lds<D, kBC, kThreads>(rk, 0, sm.k[0], tid);
-  tile_to_lds<D, kBC, kThreads>(rv, 0, sm.v[0], tid);
+  tile_to_lds<D, kBC, kThreads>(rk, 0, k0s, tid);
+  tile_to_lds<D, kBC, kThreads>(rv, 0, v0s, tid);
   wait_vmem_all();
   __syncthreads();
 
-  for (int j = 0; j < ntiles; ++j) {
-    const int buf = j & 1;
-    const bool more = j + 1 < ntiles;
-    if (more) {
-      tile_to_lds<D, kBC, kThreads>(rk, (j + 1) * kBC, sm.k[buf ^ 1], tid);
-      tile_to_lds<D, kBC, kThreads>(rv, (j + 1) * kBC, sm.v[buf ^ 1], tid);
+  // One key tile; P is its parity (compile-time), the tile is in buffers P, buffers P^1 are free.
+  auto tile_fn = [&](auto parity, int j) {
+    constexpr int P = decltype(parity)::value;
+    if (j + 1 < ntiles) {
+      tile_to_lds<D, kBC, kThreads>(rk, (j + 1) * kBC, P ? k0s : k1s, tid);
+      tile_to_lds<D, kBC, kThreads>(rv, (j + 1) * kBC, P ? v0s : v1s, tid);
     }
     const int kv0 = j * kBC;
     if (!(CAUSAL && kv0 > qw + 31)) {
-      const bf16* klds = sm.k[buf];
-      const bf16* vlds = sm.v[buf];
+      const char* klds = (const char*)(P ? k1s : k0s);
+      const char* vlds = (const char*)(P ? v1s : v0s);
       f32x16 sacc[2], pacc[2];  // Sᵀ and dPᵀ: element (kb, r) is key kv0 + 32kb + 8(r/4) + 4g + r%4
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
@@ -314,14 +313,14 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
           sacc[kb][r] = 0.f;
           pacc[kb][r] = 0.f;
         }
-#pragma unroll
-        for (int s = 0; s < KSTEPS; ++s) {
-          const bf16x8 ka = *(const bf16x8*)&klds[tile_off<D>(kb * 32 + lc, 16 * s + 8 * g)];
-          const bf16x8 va = *(const bf16x8*)&vlds[tile_off<D>(kb * 32 + lc, 16 * s + 8 * g)];
-          sacc[kb] = mfma_32x32x16(ka, qf[s], sacc[kb]);
-          pacc[kb] = mfma_32x32x16(va, df[s], pacc[kb]);
-        }
       }
+#pragma unroll
+      for (int s = 0; s < KSTEPS; ++s)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          sacc[kb] = mfma_32x32x16(row_frag<D>(klds, fo, kb, s), qf[s], sacc[kb]);
+          pacc[kb] = mfma_32x32x16(row_frag<D>(vlds, fo, kb, s), df[s], pacc[kb]);
+        }
       const bool need_mask = (kv0 + kBC > N) || (CAUSAL && kv0 + kBC - 1 > qw);
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -342,20 +341,18 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
 #pragma unroll
         for (int e = 0; e < 8; ++e) dsf[ks][e] = (__bf16)pacc[ks >> 1][8 * (ks & 1) + e];
 #pragma unroll
-      for (int b = 0; b < DB; ++b) {
+      for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-          const int key = 16 * ks + 4 * g + tr_a;
-          const int col = 32 * b + tr_n + 4 * tr_b;
-          const u32x2 lo = lds_read_tr16(&klds[tile_off<D>(key, col)]);
-          const u32x2 hi = lds_read_tr16(&klds[tile_off<D>(key + 8, col)]);
-          const u32x4 kk = {lo[0], lo[1], hi[0], hi[1]};
-          qacc[b] = mfma_32x32x16(__builtin_bit_cast(bf16x8, kk), dsf[ks], qacc[b]);
-        }
-      }
+        for (int b = 0; b < DB; ++b)
+          qacc[b] = mfma_32x32x16(tr_frag<D>(klds, fo, ks, b), dsf[ks], qacc[b]);
     }
     wait_vmem_all();
     __syncthreads();
+  };
+
+  for (int j = 0; j < ntiles; j += 2) {
+    tile_fn(std::integral_constant<int, 0>{}, j);
+    if (j + 1 < ntiles) tile_fn(std::integral_constant<int, 1>{}, j + 1);
   }
 
   if (qi < N) {

@@ -95,13 +95,65 @@ __device__ inline uint32_t pack_bf16x2(float lo, float hi) {
 __device__ inline float bf16_bits_to_float(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
 
 // LDS tile layout for a [rows][D] bf16 tile with no padding: the 16-byte chunk c of row r is stored at
-// chunk c ^ f(r), f(r) = ((r & 3) << 1) | ((r >> 2) & 1).  With 32 four-byte banks this keeps both
-// access patterns the kernels use conflict-free: 8 lanes reading 16 bytes from 8 consecutive rows of
-// one chunk, and 16 lanes of a transposed read covering 4 consecutive rows × 32 bytes.
-__device__ inline int swz_f(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
+// chunk c ^ H(r).  gfx950's LDS has 64 four-byte banks and serves 16 lanes of a 16-byte read (32 lanes
+// of an 8-byte read) per pass; H is chosen so both access patterns the kernels use are conflict-free:
+//   * row reads: 16 lanes read the same logical chunk of 16 consecutive rows — H(r) takes every value
+//     once over any 16 consecutive rows;
+//   * transposed reads: 32 lanes read 4 consecutive rows × 64 bytes — the 4 rows' chunk groups land
+//     on disjoint bank quarters.
+// D = 128 (256-byte rows): H(r) = 4·(r mod 4) + (r/4 mod 4).
+// D = 64 (128-byte rows, two rows per bank period): H(r) = 4·(r/2 mod 2) + (r/4 mod 4).
+template <int D>
+__device__ inline int swz_h(int r) {
+  if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
+  else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+}
 template <int D>
 __device__ inline int tile_off(int row, int col) {
-  return row * D + ((((col >> 3) ^ swz_f(row)) << 3) | (col & 7));
+  return row * D + ((((col >> 3) ^ swz_h<D>(row)) << 3) | (col & 7));
+}
+
+// Per-lane LDS byte offsets of the matrix-core fragments a lane reads from a tile in the tile_off<D>
+// layout.  H depends only on a row's low 4 bits, so a fragment 16 or 32 rows further down is the same
+// lane offset plus a compile-time constant (folded into the read's immediate offset).
+template <int D>
+struct FragOffsets {
+  // Row read (16 bytes) of row 32kb + (lane % 32), d = 16s + 8g .. +7:  row[s] + 64·D·kb.
+  uint32_t row[D / 16];
+  // Transposed read (8 bytes) of rows 16ks + 8h + 4g + tr_a, d = 32b + tr_n + 4 tr_b .. +3:
+  // tr[b][h] + 32·D·ks.
+  uint32_t tr[D / 32][2];
+  __device__ explicit FragOffsets(int lane) {
+    const int g = lane >> 5, lc = lane & 31;
+    const int tr_a = (lane & 15) >> 2, tr_b = lane & 3, tr_n = 16 * ((lane >> 4) & 1);
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s)
+      row[s] = (uint32_t)(lc * D * 2 + 16 * ((2 * s + g) ^ swz_h<D>(lc)));
+    const int x = tr_n / 8 + (tr_b >> 1);
+#pragma unroll
+    for (int b = 0; b < D / 32; ++b)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int r = 4 * g + tr_a + 8 * h;
+        tr[b][h] = (uint32_t)(r * D * 2 + 16 * ((4 * b + x) ^ swz_h<D>(r)) + 8 * (tr_b & 1));
+      }
+  }
+};
+
+// A-/B-operand fragment with 8 consecutive d values: row 32kb + (lane % 32), d = 16s + 8g .. +7.
+template <int D>
+__device__ inline bf16x8 row_frag(const char* lds, const FragOffsets<D>& fo, int kb, int s) {
+  return *(const bf16x8*)(lds + fo.row[s] + kb * 64 * D);
+}
+
+// Operand fragment whose contraction index runs down the tile's rows: column d = 32b + (lane % 32),
+// slots e = 0..7 hold rows 16ks + 4g + 8(e/4) + (e%4).
+template <int D>
+__device__ inline bf16x8 tr_frag(const char* lds, const FragOffsets<D>& fo, int ks, int b) {
+  const u32x2 lo = lds_read_tr16((const bf16*)(lds + fo.tr[b][0] + ks * 32 * D));
+  const u32x2 hi = lds_read_tr16((const bf16*)(lds + fo.tr[b][1] + ks * 32 * D));
+  const u32x4 v = {lo[0], lo[1], hi[0], hi[1]};
+  return __builtin_bit_cast(bf16x8, v);
 }
 
 // Asynchronous copy of a [ROWS][D] bf16 tile (rows row0 .. row0+ROWS-1 of a [*, D] matrix behind the
@@ -119,7 +171,7 @@ __device__ inline void tile_to_lds(__amdgpu_buffer_rsrc_t r, int row0, bf16* lds
     const int blk = i * (NT / 64) + wave;  // 1 KB block of the tile written by this wave
     const int slot = blk * 64 + lane;      // physical 16-byte slot
     const int row = slot / CPR, pc = slot % CPR;
-    const int c = pc ^ swz_f(row);         // logical chunk held by physical chunk pc
+    const int c = pc ^ swz_h<D>(row);      // logical chunk held by physical chunk pc
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
         r, (__attribute__((address_space(3))) void*)(lds + blk * 512), 16,
         (uint32_t)((row0 + row) * D + 8 * c) * 2u, 0, 0, 0);

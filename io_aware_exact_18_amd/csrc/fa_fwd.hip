@@ -7,21 +7,27 @@
 //
 // Work split (gfx950, wave64):
 //   * 4 waves per workgroup, 32 queries per wave: B_r = 128.  Key/value tiles of B_c = 64 rows are
-//     copied straight from memory into LDS (buffer_load ... lds; double-buffered, one barrier per
-//     tile, XOR-swizzled rows) and shared by the 4 waves.
+//     copied straight from memory into LDS (buffer_load ... lds, XOR-swizzled rows) and shared by the
+//     4 waves; one barrier per tile.
 //   * Each wave computes the transposed score tile Sᵀ = K Qᵀ on the 32×32×16 bf16 matrix core, so
 //     every lane owns one query column: the row maximum and row sum of the softmax are in-lane
 //     reductions plus one exchange between the two half-waves (v_permlane32_swap).
 //   * The probabilities leave the accumulator as bf16 and feed Oᵀ += Vᵀ Pᵀ directly as the B
 //     operand; V is read from its row-major LDS tile with ds_read_b64_tr_b16, whose key order matches
 //     the accumulator's row order, so P never goes through LDS.
+//   * Software pipeline: K tiles are staged one tile ahead of V tiles, so while the vector units run
+//     the softmax of tile j the matrix cores already compute the scores of tile j + 1 (the overlap of
+//     matrix products with the softmax that "Anatomy ...", section "What changed between
+//     FlashAttention 1, 2, and 3?", credits for FA3's speed, done here within one wave).
 //   * The softmax runs in base 2 with scale·log2(e) folded into one FMA; normalisation by the row sum
-//     is deferred to the end (fewer non-matmul operations, "Anatomy ...", section "What changed
-//     between FlashAttention 1, 2, and 3?").  LSE is converted back to natural log on output.
+//     is deferred to the end (fewer non-matmul operations, same section).  LSE is converted back to
+//     natural log on output.
 //   * Grid: one workgroup per (batch·head, query tile); query tiles of one head are kept on one XCD so
 //     the head's K/V stay in that XCD's L2; under the causal mask the heaviest tiles start first.
 #include "fa_common.h"
 #include "fa_launch.h"
+
+#include <type_traits>
 
 namespace fa {
 namespace {
@@ -30,25 +36,44 @@ constexpr int kBR = 128;   // queries per workgroup
 constexpr int kBC = 64;    // keys per tile
 constexpr int kThreads = 256;
 
+
+// Sᵀ = K Qᵀ for one 64-key tile: acc[kb] element r is key 32kb + 8(r/4) + 4g + (r%4) of the tile,
+// query = this lane's query.  The two key blocks' chains are interleaved and each K fragment is read
+// two products ahead of its use.
 template <int D>
-struct FwdSmem {
-  bf16 k[2][kBC * D];  // swizzled with tile_off<D>
-  bf16 v[2][kBC * D];
-};
+__device__ inline void scores_tile(const char* klds, const FragOffsets<D>& fo,
+                                   const bf16x8 (&qf)[D / 16], f32x16 (&acc)[2]) {
+  constexpr int NS = D / 16;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[kb][r] = 0.f;
+  bf16x8 f[2 * NS];
+#pragma unroll
+  for (int i = 0; i < 2 * NS; ++i) f[i] = row_frag<D>(klds, fo, i & 1, i >> 1);
+#pragma unroll
+  for (int i = 0; i < 2 * NS; ++i) acc[i & 1] = mfma_32x32x16(f[i], qf[i >> 1], acc[i & 1]);
+}
 
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     bf16* __restrict__ O, float* __restrict__ LSE, int N, int nqt, float scale_log2, int remap) {
-  constexpr int KSTEPS = D / 16;                 // k-steps of the Sᵀ product
-  constexpr int DB = D / 32;                     // 32-row blocks of Oᵀ
-  __shared__ FwdSmem<D> sm;
+  constexpr int KSTEPS = D / 16;  // k-steps of the Sᵀ product
+  constexpr int DB = D / 32;      // 32-row blocks of Oᵀ
+  // K(j) lives in k<j % 2>, V(j) in v<j % 2> (tile_off<D> layout).  Four separate LDS objects, so the
+  // compiler can tell the buffer being read from the one an in-flight LDS-DMA copy is writing and
+  // does not wait for the copy before unrelated reads.
+  __shared__ __attribute__((aligned(1024))) bf16 k0s[kBC * D];
+  __shared__ __attribute__((aligned(1024))) bf16 k1s[kBC * D];
+  __shared__ __attribute__((aligned(1024))) bf16 v0s[kBC * D];
+  __shared__ __attribute__((aligned(1024))) bf16 v1s[kBC * D];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int g = lane >> 5;        // half-wave: selects k-slots 8g..8g+7
-  const int lc = lane & 31;       // row / column index inside a 32-wide matrix-core tile
+  const int g = lane >> 5;   // half-wave: selects k-slots 8g..8g+7
+  const int lc = lane & 31;  // row / column index inside a 32-wide matrix-core tile
 
   const uint32_t total = gridDim.x;
   const uint32_t logical = remap ? xcd_remap(blockIdx.x, total) : blockIdx.x;
@@ -73,11 +98,20 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
 
   const int kv_end = CAUSAL ? min(N, q0 + kBR) : N;
   const int ntiles = (kv_end + kBC - 1) / kBC;
+  // Tiles at or beyond this index are fully masked for this wave (causal): no math on them.
+  const int wave_tiles = CAUSAL ? min(ntiles, (qw + 31) / kBC + 1) : ntiles;
+  const FragOffsets<D> fo(lane);
 
-  tile_to_lds<D, kBC, kThreads>(rk, 0, sm.k[0], tid);
-  tile_to_lds<D, kBC, kThreads>(rv, 0, sm.v[0], tid);
+  // Prologue: K(0), K(1), V(0) in flight; scores of tile 0.
+  tile_to_lds<D, kBC, kThreads>(rk, 0, k0s, tid);
+  if (ntiles > 1) tile_to_lds<D, kBC, kThreads>(rk, kBC, k1s, tid);
+  tile_to_lds<D, kBC, kThreads>(rv, 0, v0s, tid);
   wait_vmem_all();
   __syncthreads();
+
+  f32x16 s_cur[2], s_nxt[2];
+  scores_tile<D>((const char*)k0s, fo, qf, s_cur);
+  __syncthreads();  // every wave is done with k[0] before K(2) overwrites it
 
   float m = -INFINITY;  // running max of the base-2 scaled scores
   float l = 0.f;        // running sum of 2^(t - m) over this lane's keys (half of the row)
@@ -87,35 +121,18 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[b][r] = 0.f;
 
-  // Transposed-read addressing for the Vᵀ operand (see fa_common.h): lane i = 4a + b of each 16-lane
-  // group reads keys k0 + a, d columns n0 + 4b .. n0 + 4b + 3.
-  const int tr_a = (lane & 15) >> 2;
-  const int tr_b = lane & 3;
-  const int tr_n = 16 * ((lane >> 4) & 1);
-
-  for (int j = 0; j < ntiles; ++j) {
-    const int buf = j & 1;
-    const bool more = j + 1 < ntiles;
-    if (more) {  // next tile streams into the other buffer while this one is used
-      tile_to_lds<D, kBC, kThreads>(rk, (j + 1) * kBC, sm.k[buf ^ 1], tid);
-      tile_to_lds<D, kBC, kThreads>(rv, (j + 1) * kBC, sm.v[buf ^ 1], tid);
-    }
+  // One tile; P is the parity of j, a compile-time constant so every LDS address below is a lane
+  // base plus an immediate.  Buffers on entry: k[P^1] = K(j+1), v[P] = V(j); k[P], v[P^1] are free.
+  auto tile = [&](auto parity, int j) {
+    constexpr int P = decltype(parity)::value;
+    bf16* const k_this = P ? k1s : k0s;   // free: receives K(j+2)
+    bf16* const k_next = P ? k0s : k1s;   // holds K(j+1)
+    bf16* const v_this = P ? v1s : v0s;   // holds V(j)
+    bf16* const v_next = P ? v0s : v1s;   // free: receives V(j+1)
+    if (j + 2 < ntiles) tile_to_lds<D, kBC, kThreads>(rk, (j + 2) * kBC, k_this, tid);
+    if (j + 1 < ntiles) tile_to_lds<D, kBC, kThreads>(rv, (j + 1) * kBC, v_next, tid);
     const int kv0 = j * kBC;
-
-    if (!(CAUSAL && kv0 > qw + 31)) {  // tile fully masked for this wave: skip the math
-      const bf16* klds = sm.k[buf];
-      const bf16* vlds = sm.v[buf];
-      f32x16 sacc[2];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
-#pragma unroll
-        for (int s = 0; s < KSTEPS; ++s) {
-          const bf16x8 kf = *(const bf16x8*)&klds[tile_off<D>(kb * 32 + lc, 16 * s + 8 * g)];
-          sacc[kb] = mfma_32x32x16(kf, qf[s], sacc[kb]);
-        }
-      }
+    if (j < wave_tiles) {
       // Accumulator element (kb, r) is key kv0 + 32kb + 8(r/4) + 4g + (r%4) for query qi.
       const bool need_mask = (kv0 + kBC > N) || (CAUSAL && kv0 + kBC - 1 > qw);
       if (need_mask) {
@@ -124,31 +141,22 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int key = kv0 + 32 * kb + 8 * (r >> 2) + 4 * g + (r & 3);
-            if (key >= N || (CAUSAL && key > qi)) sacc[kb][r] = -INFINITY;
+            if (key >= N || (CAUSAL && key > qi)) s_cur[kb][r] = -INFINITY;
           }
       }
-      float mx = sacc[0][0];
+      float mx = fmaxf(s_cur[0][0], s_cur[1][0]);
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s_cur[kb][r]);
       mx = halves_max(mx);
       const float m_new = fmaxf(m, mx * scale_log2);
       const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = exp2_fast(m - m_use);
-      float rs[4] = {0.f, 0.f, 0.f, 0.f};  // four partial sums: shorter dependency chains
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float p = exp2_fast(fmaf(sacc[kb][r], scale_log2, -m_use));
-          sacc[kb][r] = p;
-          rs[r & 3] += p;
-        }
-      l = fmaf(l, alpha, (rs[0] + rs[1]) + (rs[2] + rs[3]));
       // Rescale the output accumulator only when some row's maximum moved (alpha != 1 somewhere in
       // the wave); once the maxima settle, most tiles skip these multiplies.
       if (!wave_all(m_new == m)) {
+        const float alpha = exp2_fast(m - m_use);
+        l *= alpha;
 #pragma unroll
         for (int b = 0; b < DB; ++b)
 #pragma unroll
@@ -156,29 +164,48 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
       }
       m = m_new;
 
+      // One branch-free block: the scores of tile j + 1 on the matrix cores (on a wave's last tile
+      // they read a stale buffer and are discarded) and the exponentials of tile j on the vector
+      // units; the group barriers at its end interleave the two streams.
+      scores_tile<D>((const char*)k_next, fo, qf, s_nxt);
+      float rs[4] = {0.f, 0.f, 0.f, 0.f};  // four partial sums: shorter dependency chains
+      bf16x8 pf[4];
       // Pᵀ operand for k-step ks (16 keys): slots e = registers 8(ks%2) + e of key block ks/2, i.e.
       // keys 16ks + 8(e/4) + 4g + (e%4) — the order the transposed V reads below produce.
-      bf16x8 pf[4];
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) pf[ks][e] = (__bf16)sacc[ks >> 1][8 * (ks & 1) + e];
-
-#pragma unroll
-      for (int b = 0; b < DB; ++b) {
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-          const int key = 16 * ks + 4 * g + tr_a;
-          const int col = 32 * b + tr_n + 4 * tr_b;
-          const u32x2 lo = lds_read_tr16(&vlds[tile_off<D>(key, col)]);
-          const u32x2 hi = lds_read_tr16(&vlds[tile_off<D>(key + 8, col)]);
-          const u32x4 vv = {lo[0], lo[1], hi[0], hi[1]};
-          oacc[b] = mfma_32x32x16(__builtin_bit_cast(bf16x8, vv), pf[ks], oacc[b]);
+        for (int e = 0; e < 8; ++e) {
+          const float p = exp2_fast(fmaf(s_cur[ks >> 1][8 * (ks & 1) + e], scale_log2, -m_use));
+          rs[e & 3] += p;
+          pf[ks][e] = (__bf16)p;
         }
+      l += (rs[0] + rs[1]) + (rs[2] + rs[3]);
+#pragma unroll
+      for (int i = 0; i < 2 * KSTEPS; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one matrix-core op
+        __builtin_amdgcn_sched_group_barrier(0x002, 7, 0);  // seven vector ALU ops
       }
+
+      const char* vlds = (const char*)v_this;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        bf16x8 vf[DB];
+#pragma unroll
+        for (int b = 0; b < DB; ++b) vf[b] = tr_frag<D>(vlds, fo, ks, b);
+#pragma unroll
+        for (int b = 0; b < DB; ++b) oacc[b] = mfma_32x32x16(vf[b], pf[ks], oacc[b]);
+      }
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) s_cur[kb] = s_nxt[kb];
     }
     wait_vmem_all();
     __syncthreads();
+  };
+
+  for (int j = 0; j < ntiles; j += 2) {
+    tile(std::integral_constant<int, 0>{}, j);
+    if (j + 1 < ntiles) tile(std::integral_constant<int, 1>{}, j + 1);
   }
 
   // Epilogue: combine the two half-row sums, normalise, write O and LSE.
