@@ -1,7 +1,302 @@
-// fa_fwd_fp8.hip — e4m3 forward kernel for gfx950 (placeholder until the fp8 kernel lands).
+// fa_fwd_fp8.hip — forward kernel with FP8 (OCP e4m3fn) matrix products for gfx950, head dim 128.
+//
+// Same method as the bf16 forward ("Anatomy of a FlashAttention Kernel", sections "Why is attention
+// memory-bound ..." and "What is online softmax ..."), with the low-precision FP8 products that the
+// section "What changed between FlashAttention 1, 2, and 3?" credits to FA3.  Q, K, V arrive as e4m3
+// codes with one fp32 descale per tensor (value = code · descale).
+//
+//   * Sᵀ = K Qᵀ on v_mfma_f32_32x32x64_f8f6f4 (fp32 accumulation; products of e4m3 values are exact).
+//     The descales and scale·log2(e) fold into the one FMA that forms the exponent.
+//   * P = 2^(s − m + 8) ∈ [0, 256] is rounded to e4m3 (v_cvt_pk_fp8_f32: round-to-nearest-even,
+//     saturating at 448) and Oᵀ += Vᵀ Pᵀ runs on the same fp8 matrix core.  The factor 2^8 (free: it
+//     is part of the FMA's constant) keeps small probabilities out of e4m3's subnormal range; it
+//     cancels in O = Σ P V / Σ P and is removed from LSE.  The row sum l is formed by one more
+//     matrix-core op against an all-ones operand, so it sums exactly the rounded P values that enter
+//     P·V.
+//   * Key order: each wave loads K rows into the A operand with bits 2 and 3 of the row index swapped,
+//     so that every lane's 32 probabilities form four runs of 8 consecutive keys; V is then read with
+//     ds_read_b64_tr_b8, which hands each lane 8 consecutive key rows of one column, and the P bytes
+//     go straight from the score accumulator into the B operand.
+//   * Tiles: 4 waves × 32 queries per workgroup, 64-key K/V tiles copied into LDS by buffer→LDS DMA,
+//     K one tile ahead of V, double-buffered, rows XOR-swizzled for conflict-free reads.
 #include "fa_common.h"
 #include "fa_launch.h"
 
+#include <type_traits>
+
 namespace fa {
-hipError_t launch_fwd_fp8(const Fp8FwdArgs&, hipStream_t) { return hipErrorNotSupported; }
+namespace {
+
+constexpr int kD = 128;
+constexpr int kBR = 128;
+constexpr int kBC = 64;
+constexpr int kThreads = 256;
+constexpr int kRowBytes = kD;  // one e4m3 byte per element
+constexpr float kPExp = 8.f;   // P is formed as 2^(s − m + kPExp)
+
+// Swizzle of 16-byte chunks within a 128-byte fp8 row (64 banks; two rows per bank period): keeps
+// 16-lane row reads and 32-lane 8-byte transposed reads conflict-free.
+__device__ inline int swz8(int r) { return (((r >> 1) & 3) << 1) | ((r >> 3) & 1); }
+
+// Rows 32kb + i of the A operand hold K row 32kb + perm(i): bits 2 and 3 of i swapped.
+__device__ inline int perm23(int i) { return (i & ~0xC) | ((i >> 1) & 4) | ((i << 1) & 8); }
+
+template <int ROWS>
+__device__ inline void tile8_to_lds(__amdgpu_buffer_rsrc_t r, int row0, uint8_t* lds, int tid) {
+  constexpr int CPR = kRowBytes / 16;
+  constexpr int CHUNKS = ROWS * CPR;
+  static_assert(CHUNKS % kThreads == 0, "tile must split evenly");
+  const int wave = tid >> 6, lane = tid & 63;
+#pragma unroll
+  for (int i = 0; i < CHUNKS / kThreads; ++i) {
+    const int blk = i * (kThreads / 64) + wave;
+    const int slot = blk * 64 + lane;
+    const int row = slot / CPR, pc = slot % CPR;
+    const int c = pc ^ swz8(row);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        r, (__attribute__((address_space(3))) void*)(lds + blk * 1024), 16,
+        (uint32_t)((row0 + row) * kRowBytes + 16 * c), 0, 0, 0);
+  }
+}
+
+__device__ inline f32x16 mfma_f8(i32x8 a, i32x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+__device__ inline u32x2 lds_read_tr8(const uint8_t* p) {
+  typedef int i32x2_t __attribute__((ext_vector_type(2)));
+  i32x2_t r = __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) i32x2_t*)(p));
+  return __builtin_bit_cast(u32x2, r);
+}
+
+// Four fp32 values → four e4m3 bytes (round to nearest even, saturating), first in the lowest byte.
+__device__ inline uint32_t pack_e4m3x4(float p0, float p1, float p2, float p3) {
+  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, 0, false);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, lo, true);
+}
+
+template <bool CAUSAL>
+__global__ __launch_bounds__(kThreads, 2) void fwd_fp8_kernel(
+    const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K, const uint8_t* __restrict__ V,
+    bf16* __restrict__ O, float* __restrict__ LSE, int N, int nqt, float c_log2, float v_descale,
+    int remap) {
+  __shared__ __attribute__((aligned(1024))) uint8_t k0s[kBC * kRowBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t k1s[kBC * kRowBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t v0s[kBC * kRowBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t v1s[kBC * kRowBytes];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int g = lane >> 5;
+  const int lc = lane & 31;
+
+  const uint32_t logical = remap ? xcd_remap(blockIdx.x, gridDim.x) : blockIdx.x;
+  const int bh = logical / nqt;
+  int qt = logical % nqt;
+  if (CAUSAL) qt = nqt - 1 - qt;
+  const int q0 = qt * kBR;
+  const int qw = q0 + 32 * wave;
+  const int qi = qw + lc;
+
+  const size_t head = (size_t)bh * N * kD;
+  const uint32_t head_bytes = (uint32_t)N * kRowBytes;
+  const auto rq = make_rsrc(Q + head, head_bytes);
+  const auto rk = make_rsrc(K + head, head_bytes);
+  const auto rv = make_rsrc(V + head, head_bytes);
+
+  // Qᵀ operand (B): this lane's query, k-step s covers d = 64s + 32g .. +31.
+  i32x8 qf[2];
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    const uint32_t off = (uint32_t)(qi * kRowBytes + 64 * s + 32 * g);
+    const u32x4 lo = buf_load16(rq, off), hi = buf_load16(rq, off + 16);
+    qf[s] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                  (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+  }
+
+  // Per-lane LDS offsets.  K rows (A operand): row perm23(lc) (+32 per key block), chunks 4s+2g+h.
+  uint32_t koff[2][2];
+  {
+    const int r = perm23(lc);
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        koff[s][h] = (uint32_t)(r * kRowBytes + 16 * ((4 * s + 2 * g + h) ^ swz8(r)));
+  }
+  // V transposed reads: the 16-lane group's lane i = 2a + b reads row k0 + a, bytes n0 + 8b .. +7
+  // with k0 = 16c + 8g and n0 = 32db + 16·((lane >> 4) & 1); the lane receives column n0 + (i) of
+  // rows k0 .. k0 + 7.  voff[db] is the offset for c = 0 (c adds 16 rows).
+  uint32_t voff[4];
+  {
+    const int a = (lane & 15) >> 1, b = lane & 1, u = (lane >> 4) & 1;
+    const int r = 8 * g + a;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+      voff[db] = (uint32_t)(r * kRowBytes + 16 * ((2 * db + u) ^ swz8(r)) + 8 * b);
+  }
+
+  const int kv_end = CAUSAL ? min(N, q0 + kBR) : N;
+  const int ntiles = (kv_end + kBC - 1) / kBC;
+  const int wave_tiles = CAUSAL ? min(ntiles, (qw + 31) / kBC + 1) : ntiles;
+
+  tile8_to_lds<kBC>(rk, 0, k0s, tid);
+  if (ntiles > 1) tile8_to_lds<kBC>(rk, kBC, k1s, tid);
+  tile8_to_lds<kBC>(rv, 0, v0s, tid);
+  wait_vmem_all();
+  __syncthreads();
+
+  auto scores = [&](const uint8_t* klds, f32x16 (&acc)[2]) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[kb][r] = 0.f;
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const u32x4 lo = *(const u32x4*)(klds + koff[s][0] + kb * 32 * kRowBytes);
+        const u32x4 hi = *(const u32x4*)(klds + koff[s][1] + kb * 32 * kRowBytes);
+        const i32x8 kf = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                          (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+        acc[kb] = mfma_f8(kf, qf[s], acc[kb]);
+      }
+    }
+  };
+
+  f32x16 s_cur[2], s_nxt[2];
+  scores(k0s, s_cur);
+  __syncthreads();
+
+  float m = -INFINITY;
+  f32x16 oacc[4], lacc;
+#pragma unroll
+  for (int b = 0; b < 4; ++b)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) oacc[b][r] = 0.f;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) lacc[r] = 0.f;
+  const i32x8 ones = {0x38383838, 0x38383838, 0x38383838, 0x38383838,
+                      0x38383838, 0x38383838, 0x38383838, 0x38383838};  // e4m3 1.0
+
+  auto tile = [&](auto parity, int j) {
+    constexpr int P = decltype(parity)::value;
+    uint8_t* const k_this = P ? k1s : k0s;
+    uint8_t* const k_next = P ? k0s : k1s;
+    uint8_t* const v_this = P ? v1s : v0s;
+    uint8_t* const v_next = P ? v0s : v1s;
+    if (j + 2 < ntiles) tile8_to_lds<kBC>(rk, (j + 2) * kBC, k_this, tid);
+    if (j + 1 < ntiles) tile8_to_lds<kBC>(rv, (j + 1) * kBC, v_next, tid);
+    const int kv0 = j * kBC;
+    if (j < wave_tiles) {
+      // Accumulator element (kb, r), r = 4q + t, is key kv0 + 32kb + 16(q/2) + 8g + 4(q%2) + t.
+      const bool need_mask = (kv0 + kBC > N) || (CAUSAL && kv0 + kBC - 1 > qw);
+      if (need_mask) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int q = r >> 2, t = r & 3;
+            const int key = kv0 + 32 * kb + 16 * (q >> 1) + 8 * g + 4 * (q & 1) + t;
+            if (key >= N || (CAUSAL && key > qi)) s_cur[kb][r] = -INFINITY;
+          }
+      }
+      float mx = fmaxf(s_cur[0][0], s_cur[1][0]);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s_cur[kb][r]);
+      mx = halves_max(mx);
+      const float m_new = fmaxf(m, mx * c_log2);
+      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+      const float m_off = m_use - kPExp;  // exponent offset: P = 2^(s·c − m + 8)
+      if (!wave_all(m_new == m)) {
+        const float alpha = exp2_fast(m - m_use);
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[b][r] *= alpha;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) lacc[r] *= alpha;
+      }
+      m = m_new;
+
+      scores(k_next, s_nxt);  // next tile's scores; discarded on the wave's last tile
+      // Pᵀ operand (B): byte e of the 8 registers is P for accumulator element (e/16, e%16), i.e.
+      // key 16(e/8) + 8g + (e%8) of the tile.
+      i32x8 pf;
+#pragma unroll
+      for (int w = 0; w < 8; ++w) {
+        const int kb = w >> 2, r0 = 4 * (w & 3);
+        const float p0 = exp2_fast(fmaf(s_cur[kb][r0 + 0], c_log2, -m_off));
+        const float p1 = exp2_fast(fmaf(s_cur[kb][r0 + 1], c_log2, -m_off));
+        const float p2 = exp2_fast(fmaf(s_cur[kb][r0 + 2], c_log2, -m_off));
+        const float p3 = exp2_fast(fmaf(s_cur[kb][r0 + 3], c_log2, -m_off));
+        pf[w] = (int)pack_e4m3x4(p0, p1, p2, p3);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 10, 0);
+      }
+
+      // Oᵀ += Vᵀ Pᵀ: A operand = V column 32db + lc, keys in the order of P's bytes.
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        i32x8 vf;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const u32x2 t8 = lds_read_tr8(v_this + voff[db] + c * 16 * kRowBytes);
+          vf[2 * c] = (int)t8[0];
+          vf[2 * c + 1] = (int)t8[1];
+        }
+        oacc[db] = mfma_f8(vf, pf, oacc[db]);
+      }
+      lacc = mfma_f8(ones, pf, lacc);  // every row: Σ over the tile's keys of the rounded P
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) s_cur[kb] = s_nxt[kb];
+    }
+    wait_vmem_all();
+    __syncthreads();
+  };
+
+  for (int j = 0; j < ntiles; j += 2) {
+    tile(std::integral_constant<int, 0>{}, j);
+    if (j + 1 < ntiles) tile(std::integral_constant<int, 1>{}, j + 1);
+  }
+
+  const float l = lacc[0];
+  const float inv = v_descale / l;
+  if (qi < N) {
+    bf16* orow = O + head + (size_t)qi * kD;
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        u32x2 w;
+        w[0] = pack_bf16x2(oacc[b][4 * r4 + 0] * inv, oacc[b][4 * r4 + 1] * inv);
+        w[1] = pack_bf16x2(oacc[b][4 * r4 + 2] * inv, oacc[b][4 * r4 + 3] * inv);
+        *(u32x2*)&orow[32 * b + 8 * r4 + 4 * g] = w;
+      }
+    if (g == 0) LSE[(size_t)bh * N + qi] = (m - kPExp + __log2f(l)) * kLn2;
+  }
+}
+
+template <bool CAUSAL>
+hipError_t launch(const Fp8FwdArgs& a, hipStream_t stream) {
+  const int nqt = (a.N + kBR - 1) / kBR;
+  const uint32_t total = (uint32_t)a.B * a.H * nqt;
+  const int remap = (total % 8u == 0u) ? 1 : 0;
+  const float c_log2 = a.scale * a.q_descale * a.k_descale * kLog2e;
+  hipLaunchKernelGGL((fwd_fp8_kernel<CAUSAL>), dim3(total), dim3(kThreads), 0, stream,
+                     (const uint8_t*)a.q8, (const uint8_t*)a.k8, (const uint8_t*)a.v8, (bf16*)a.o,
+                     a.lse, a.N, nqt, c_log2, a.v_descale, remap);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_fwd_fp8(const Fp8FwdArgs& a, hipStream_t stream) {
+  return a.causal ? launch<true>(a, stream) : launch<false>(a, stream);
+}
+
 }  // namespace fa
