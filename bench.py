@@ -26,6 +26,7 @@ sys.path.insert(0, ROOT)
 METRIC = "attention TFLOP/s fwd+bwd (bf16, d=128, N=4096 causal) and % of MFMA peak"
 # MI355X published dense peaks: 256 CUs × 2.4 GHz; bf16 matrix cores 4096 FLOP/clk/CU.
 BF16_PEAK_TFLOPS = 256 * 2.4e9 * 4096 / 1e12     # 2516.6
+FP8_PEAK_TFLOPS = 2 * BF16_PEAK_TFLOPS            # 5033.2 (dense e4m3 matrix cores)
 HBM_PEAK_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
@@ -89,6 +90,41 @@ def cpu_baseline(w, inp, budget_s):
     }
 
 
+def fp8_forward(fa, workloads, lib, steps, warmup):
+    """Secondary measurement: the FP8 forward on its workload (fp8_8k), timed with events."""
+    import torch
+    w = workloads.WORKLOADS["fp8_8k"]
+    B, H, N, d = w.shape()
+    log(f"[bench] secondary: {w.name} fp8 forward B={B} H={H} N={N} d={d} causal={w.causal}")
+    inp = workloads.make_inputs(w.name)
+    dev = torch.device("cuda:0")
+    q8, k8, v8 = (inp[x].to(dev) for x in ("q8", "k8", "v8"))
+    o = torch.empty((B, H, N, d), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def run():
+        code = lib.fa_fwd_fp8(q8.data_ptr(), k8.data_ptr(), v8.data_ptr(), inp["sq"], inp["sk"],
+                              inp["sv"], o.data_ptr(), lse.data_ptr(), B, H, N, d, int(w.causal),
+                              w.scale, stream.cuda_stream)
+        if code != 0:
+            raise fa.FaError("fa_fwd_fp8", code, fa.status_str(code))
+
+    for _ in range(warmup):
+        run()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record(stream)
+    for _ in range(steps):
+        run()
+    ev[1].record(stream)
+    torch.cuda.synchronize(dev)
+    ms = ev[0].elapsed_time(ev[1]) / steps
+    tflops = w.fwd_flops() / (ms * 1e-3) / 1e12
+    return {"workload": w.name, "kernel": "fwd_fp8_kernel", "ms": ms, "tflops": tflops,
+            "peak": FP8_PEAK_TFLOPS, "frac": tflops / FP8_PEAK_TFLOPS, "bound": "mfma",
+            "flops": w.fwd_flops()}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -98,6 +134,8 @@ def main():
                     help="bf16 forward+backward workload (default: the throughput workload)")
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle work for the cpu_baseline leg (0 skips it)")
+    ap.add_argument("--no-fp8", action="store_true",
+                    help="skip the secondary FP8 forward measurement (fp8_8k workload)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of the bench, run a plain device copy of MIB MiB `--steps` times "
                          "(the reference kernel for scaling HBM byte counters)")
@@ -222,6 +260,10 @@ def main():
         "launch_ms": dom_k["ms"],
     }
 
+    secondary = {}
+    if not args.no_fp8:
+        secondary["fp8_8k_fwd"] = fp8_forward(fa, workloads, lib, args.steps, args.warmup)
+
     cpu = None
     if args.cpu_budget > 0:
         log(f"[bench] timing the CPU oracle for ~{args.cpu_budget:.0f} s")
@@ -250,6 +292,7 @@ def main():
         "bwd_tflops": bwd_f / ((pre_ms + dkdv_ms + dq_ms) * 1e-3) / 1e12,
         "kernels": {n: {k2: v2 for k2, v2 in kk.items() if k2 != "src"} for n, kk in kernels.items()},
         "roofline": roofline,
+        "secondary": secondary,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
