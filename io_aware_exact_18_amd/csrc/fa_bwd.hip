@@ -71,7 +71,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(
     int remap) {
   constexpr int KSTEPS = D / 16;
   constexpr int DB = D / 32;
-  // Q and dO tiles (tile_off<D> layout) and the tile's LSE and D values (first 32 of 64 used),
+  // Q and dO tiles (tile_off<D> layout) and the tile's base-2 LSE and D values (first 32 of 64 used),
   // double-buffered; separate LDS objects so reads of one buffer never wait for the LDS-DMA copy
   // filling the other.
   __shared__ __attribute__((aligned(1024))) bf16 q0s[kBQ * D];
@@ -86,7 +86,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = wave_index(tid);
   const int g = lane >> 5;
   const int lc = lane & 31;
 
@@ -99,12 +99,12 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(
 
   const size_t head = (size_t)bh * N * D;
   const uint32_t head_bytes = (uint32_t)N * D * 2u;
-  const auto rq = make_rsrc(Q + head, head_bytes);
+  const auto mq = make_rsrc(Q + head, head_bytes);
+  const auto mdo = make_rsrc(dO + head, head_bytes);
   const auto rk = make_rsrc(K + head, head_bytes);
-  const auto rv = make_rsrc(V + head, head_bytes);
-  const auto rdo = make_rsrc(dO + head, head_bytes);
   const auto rlse = make_rsrc(LSE + (size_t)bh * N, (uint32_t)N * 4u);
   const auto rdel = make_rsrc(Delta + (size_t)bh * N, (uint32_t)N * 4u);
+  const BfTileCopy<D, kBQ, kThreads> copy(tid);
 
   // Kᵀ operands (B operand of S = Q Kᵀ) in registers: column = this lane's key.  The Vᵀ operand of
   // dP = dO Vᵀ is read from the LDS copy of the workgroup's V rows each step (registers are the
@@ -113,17 +113,24 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(
 #pragma unroll
   for (int s = 0; s < KSTEPS; ++s)
     kf[s] = __builtin_bit_cast(bf16x8, buf_load16(rk, (uint32_t)(kj * D + 16 * s + 8 * g) * 2u));
-  tile_to_lds<D, kBKV, kThreads>(rv, k0, vts, tid);
+  {
+    const BfTileCopy<D, kBKV, kThreads> copy_v(tid);
+    copy_v(make_rsrc(V + head, head_bytes), k0, vts);
+  }
 
   const FragOffsets<D> fo(lane);
   const int qstart = CAUSAL ? k0 : 0;  // causal: only queries ≥ the tile's first key
   const int nsteps = (N - qstart + kBQ - 1) / kBQ;
 
-  auto stage = [&](int step, bf16* qd, bf16* od, float* ld, float* dd) {
+  // Q, dO and D of query step `step` go to LDS by DMA; wave 0 also loads the step's LSE into a
+  // register and stores it, times log2(e), to LDS just before the step's closing barrier, so the
+  // probabilities below are one FMA and one exp2 each.
+  float lse_next = 0.f;
+  auto stage = [&](int step, bf16* qd, bf16* od, float* dd) {
     const int qb = qstart + step * kBQ;
-    tile_to_lds<D, kBQ, kThreads>(rq, qb, qd, tid);
-    tile_to_lds<D, kBQ, kThreads>(rdo, qb, od, tid);
-    if (wave == 0) vec64_to_lds(rlse, qb, ld, lane);
+    copy(mq, qb, qd);
+    copy(mdo, qb, od);
+    if (wave == 0) lse_next = __uint_as_float(buf_load4(rlse, (uint32_t)(qb + lane) * 4u));
     if (wave == 1) vec64_to_lds(rdel, qb, dd, lane);
   };
 
@@ -136,8 +143,9 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(
       dva[b][r] = 0.f;
     }
 
-  stage(0, q0s, o0s, l0s, d0s);
+  stage(0, q0s, o0s, d0s);
   wait_vmem_all();
+  if (wave == 0) l0s[lane] = lse_next * kLog2e;
   __syncthreads();
 
   // One query tile; P (the step's parity) is a compile-time constant so the buffers are fixed
@@ -148,7 +156,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(
     const char* dos = (const char*)(P ? o1s : o0s);
     const float* lse_s = P ? l1s : l0s;
     const float* del_s = P ? d1s : d0s;
-    if (step + 1 < nsteps) stage(step + 1, P ? q0s : q1s, P ? o0s : o1s, P ? l0s : l1s, P ? d0s : d1s);
+    if (step + 1 < nsteps) stage(step + 1, P ? q0s : q1s, P ? o0s : o1s, P ? d0s : d1s);
     const int qb = qstart + step * kBQ;
 
     if (!(CAUSAL && kw > qb + kBQ - 1)) {  // every (query, key) pair masked for this wave: skip
@@ -165,8 +173,15 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(
         pacc = mfma_32x32x16(row_frag<D>(dos, fo, 0, s), row_frag<D>((const char*)vts, fo, wave, s),
                              pacc);
       }
-      // Element r: query qb + 8(r/4) + 4g + (r%4), key kj.
-      const bool need_mask = (kw + 31 >= N) || (CAUSAL && kw + 31 > qb);
+      // Element r: query qb + 8(r/4) + 4g + (r%4), key kj.  Masked scores become -inf (P = 0) in a
+      // wave-uniform branch taken only by diagonal and ragged tiles.
+      if ((kw + 31 >= N) || (CAUSAL && kw + 31 > qb)) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int qi = qb + 8 * (r >> 2) + 4 * g + (r & 3);
+          if (kj >= N || (CAUSAL && kj > qi)) sacc[r] = -INFINITY;
+        }
+      }
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
         const f32x4 l4 = *(const f32x4*)&lse_s[8 * r4 + 4 * g];
@@ -174,11 +189,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
           const int r = 4 * r4 + t;
-          float p = exp2_fast(fmaf(sacc[r], scale_log2, -l4[t] * kLog2e));
-          if (need_mask) {
-            const int qi = qb + 8 * r4 + 4 * g + t;
-            if (kj >= N || (CAUSAL && kj > qi)) p = 0.f;
-          }
+          const float p = exp2_fast(fmaf(sacc[r], scale_log2, -l4[t]));  // staged LSE is base 2
           sacc[r] = p;
           pacc[r] = p * (pacc[r] - d4[t]);  // dS without the scale
         }
@@ -202,6 +213,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(
       }
     }
     wait_vmem_all();
+    if (wave == 0 && step + 1 < nsteps) (P ? l0s : l1s)[lane] = lse_next * kLog2e;
     __syncthreads();
   };
 
@@ -247,7 +259,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = wave_index(tid);
   const int g = lane >> 5;
   const int lc = lane & 31;
 
@@ -262,9 +274,10 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
   const size_t head = (size_t)bh * N * D;
   const uint32_t head_bytes = (uint32_t)N * D * 2u;
   const auto rq = make_rsrc(Q + head, head_bytes);
-  const auto rk = make_rsrc(K + head, head_bytes);
-  const auto rv = make_rsrc(V + head, head_bytes);
   const auto rdo = make_rsrc(dO + head, head_bytes);
+  const auto mk = make_rsrc(K + head, head_bytes);
+  const auto mv = make_rsrc(V + head, head_bytes);
+  const BfTileCopy<D, kBC, kThreads> copy(tid);
 
   // Qᵀ and dOᵀ operands (B operands): column = this lane's query, slots d = 16s + 8g + (0..7).
   bf16x8 qf[KSTEPS], df[KSTEPS];
@@ -289,8 +302,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
 #pragma unroll
     for (int r = 0; r < 16; ++r) qacc[b][r] = 0.f;
 
-  tile_to_lds<D, kBC, kThreads>(rk, 0, k0s, tid);
-  tile_to_lds<D, kBC, kThreads>(rv, 0, v0s, tid);
+  copy(mk, 0, k0s);
+  copy(mv, 0, v0s);
   wait_vmem_all();
   __syncthreads();
 
@@ -298,8 +311,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
   auto tile_fn = [&](auto parity, int j) {
     constexpr int P = decltype(parity)::value;
     if (j + 1 < ntiles) {
-      tile_to_lds<D, kBC, kThreads>(rk, (j + 1) * kBC, P ? k0s : k1s, tid);
-      tile_to_lds<D, kBC, kThreads>(rv, (j + 1) * kBC, P ? v0s : v1s, tid);
+      copy(mk, (j + 1) * kBC, P ? k0s : k1s);
+      copy(mv, (j + 1) * kBC, P ? v0s : v1s);
     }
     const int kv0 = j * kBC;
     if (!(CAUSAL && kv0 > qw + 31)) {
@@ -321,16 +334,22 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
           sacc[kb] = mfma_32x32x16(row_frag<D>(klds, fo, kb, s), qf[s], sacc[kb]);
           pacc[kb] = mfma_32x32x16(row_frag<D>(vlds, fo, kb, s), df[s], pacc[kb]);
         }
-      const bool need_mask = (kv0 + kBC > N) || (CAUSAL && kv0 + kBC - 1 > qw);
+      // Masked scores become -inf (P = 0) in a wave-uniform branch taken only by diagonal and
+      // ragged tiles.
+      if ((kv0 + kBC > N) || (CAUSAL && kv0 + kBC - 1 > qw)) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = kv0 + 32 * kb + 8 * (r >> 2) + 4 * g + (r & 3);
+            if (key >= N || (CAUSAL && key > qi)) sacc[kb][r] = -INFINITY;
+          }
+      }
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          float p = exp2_fast(fmaf(sacc[kb][r], scale_log2, -lse2));
-          if (need_mask) {
-            const int key = kv0 + 32 * kb + 8 * (r >> 2) + 4 * g + (r & 3);
-            if (key >= N || (CAUSAL && key > qi)) p = 0.f;
-          }
+          const float p = exp2_fast(fmaf(sacc[kb][r], scale_log2, -lse2));
           pacc[kb][r] = p * (pacc[kb][r] - dlt);  // dSᵀ without the scale
         }
       // dSᵀ operand for k-step ks (16 keys): registers 8(ks%2) .. +7 of key block ks/2, i.e. keys

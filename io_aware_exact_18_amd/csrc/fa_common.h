@@ -80,6 +80,10 @@ __device__ inline float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 // against the loop's own prefetch loads and exposes their latency on every iteration.
 __device__ inline void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
 
+// Index of this thread's wave in the workgroup, as a wave-uniform (scalar) value, so conditions and
+// addresses derived from it stay in scalar registers and branches on it are uniform.
+__device__ inline int wave_index(int tid) { return __builtin_amdgcn_readfirstlane(tid >> 6); }
+
 // True when `pred` holds on every active lane of the wave (a wave-uniform answer).
 __device__ inline bool wave_all(bool pred) { return __builtin_amdgcn_ballot_w64(!pred) == 0; }
 
@@ -156,27 +160,49 @@ __device__ inline bf16x8 tr_frag(const char* lds, const FragOffsets<D>& fo, int 
   return __builtin_bit_cast(bf16x8, v);
 }
 
-// Asynchronous copy of a [ROWS][D] bf16 tile (rows row0 .. row0+ROWS-1 of a [*, D] matrix behind the
-// buffer resource `r`) into LDS in the tile_off<D> layout, by NT threads, without passing through
-// registers (buffer_load_dwordx4 ... lds: lane i of a wave writes LDS bytes [16 i, 16 i + 16) after the
-// wave-uniform base).  Rows past the buffer's end read as zeros.  Completion: wait_vmem_all().
-template <int D, int ROWS, int NT>
-__device__ inline void tile_to_lds(__amdgpu_buffer_rsrc_t r, int row0, bf16* lds, int tid) {
-  constexpr int CPR = D / 8;  // 16-byte chunks per row
-  constexpr int CHUNKS = ROWS * CPR;
-  static_assert(CHUNKS % NT == 0, "tile must split evenly over the threads");
-  const int wave = tid >> 6, lane = tid & 63;
-#pragma unroll
-  for (int i = 0; i < CHUNKS / NT; ++i) {
-    const int blk = i * (NT / 64) + wave;  // 1 KB block of the tile written by this wave
-    const int slot = blk * 64 + lane;      // physical 16-byte slot
+// Asynchronous copy of ROWS rows of ROW_BYTES bytes (rows row0 .. row0+ROWS-1 of the matrix behind
+// the buffer resource `r`) into LDS by NT threads, without passing through registers
+// (buffer_load_dwordx4 ... lds: lane i of a wave writes LDS bytes [16 i, 16 i + 16) after the
+// wave-uniform base).  Rows past the buffer's end read as zeros.  The 16-byte chunk c of row r is
+// stored at physical chunk c ^ swz(r), where swz depends only on r mod 16.  Each issue round covers
+// NT / (ROW_BYTES / 16) rows, a multiple of 16, so a lane's offset within a round is the same in every
+// round and every tile: it is computed once, here, and each load of a copy adds a scalar row offset
+// to it (one vector add; the row offset stays in the range-checked vector offset so the zero fill
+// of ragged tails still applies).  Completion: wait_vmem_all().
+template <int ROW_BYTES, int ROWS, int NT>
+struct TileCopy {
+  static constexpr int CPR = ROW_BYTES / 16;        // 16-byte chunks per row
+  static constexpr int ROUNDS = ROWS * CPR / NT;    // loads per thread
+  static constexpr int ROUND_ROWS = NT / CPR;       // rows per round
+  static_assert(ROWS * CPR % NT == 0, "tile must split evenly over the threads");
+  static_assert(ROUND_ROWS % 16 == 0, "the swizzle must repeat across rounds");
+  uint32_t voff;  // this lane's byte offset inside a round
+  int wave;
+  template <class Swz>
+  __device__ TileCopy(int tid, Swz swz) {
+    wave = wave_index(tid);
+    const int slot = wave * 64 + (tid & 63);  // physical 16-byte slot within round 0
     const int row = slot / CPR, pc = slot % CPR;
-    const int c = pc ^ swz_h<D>(row);      // logical chunk held by physical chunk pc
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        r, (__attribute__((address_space(3))) void*)(lds + blk * 512), 16,
-        (uint32_t)((row0 + row) * D + 8 * c) * 2u, 0, 0, 0);
+    voff = (uint32_t)(row * ROW_BYTES + 16 * (pc ^ swz(row)));  // logical chunk held by slot pc
   }
-}
+  template <class T>
+  __device__ void operator()(__amdgpu_buffer_rsrc_t r, int row0, T* lds) const {
+#pragma unroll
+    for (int i = 0; i < ROUNDS; ++i) {
+      const uint32_t base = (uint32_t)(row0 + i * ROUND_ROWS) * (uint32_t)ROW_BYTES;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          r, (__attribute__((address_space(3))) void*)((char*)lds + (i * (NT / 64) + wave) * 1024),
+          16, voff + base, 0, 0, 0);
+    }
+  }
+};
+
+// TileCopy for a [ROWS][D] bf16 tile in the tile_off<D> layout.
+template <int D, int ROWS, int NT>
+struct BfTileCopy : TileCopy<2 * D, ROWS, NT> {
+  __device__ explicit BfTileCopy(int tid)
+      : TileCopy<2 * D, ROWS, NT>(tid, [](int r) { return swz_h<D>(r); }) {}
+};
 
 // Asynchronous copy of 64 consecutive fp32 values (elements e0 .. e0+63 behind `r`) into LDS by one
 // wave; values past the buffer's end read as zeros.

@@ -71,7 +71,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = wave_index(tid);
   const int g = lane >> 5;   // half-wave: selects k-slots 8g..8g+7
   const int lc = lane & 31;  // row / column index inside a 32-wide matrix-core tile
 
@@ -87,8 +87,9 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
   const size_t head = (size_t)bh * N * D;
   const uint32_t head_bytes = (uint32_t)N * D * 2u;
   const auto rq = make_rsrc(Q + head, head_bytes);
-  const auto rk = make_rsrc(K + head, head_bytes);
-  const auto rv = make_rsrc(V + head, head_bytes);
+  const auto mk = make_rsrc(K + head, head_bytes);
+  const auto mv = make_rsrc(V + head, head_bytes);
+  const BfTileCopy<D, kBC, kThreads> copy(tid);
 
   // Qᵀ fragments (B operand): column = this lane's query, slots = d in [16s + 8g, 16s + 8g + 8).
   bf16x8 qf[KSTEPS];
@@ -103,9 +104,9 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
   const FragOffsets<D> fo(lane);
 
   // Prologue: K(0), K(1), V(0) in flight; scores of tile 0.
-  tile_to_lds<D, kBC, kThreads>(rk, 0, k0s, tid);
-  if (ntiles > 1) tile_to_lds<D, kBC, kThreads>(rk, kBC, k1s, tid);
-  tile_to_lds<D, kBC, kThreads>(rv, 0, v0s, tid);
+  copy(mk, 0, k0s);
+  if (ntiles > 1) copy(mk, kBC, k1s);
+  copy(mv, 0, v0s);
   wait_vmem_all();
   __syncthreads();
 
@@ -129,8 +130,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     bf16* const k_next = P ? k0s : k1s;   // holds K(j+1)
     bf16* const v_this = P ? v1s : v0s;   // holds V(j)
     bf16* const v_next = P ? v0s : v1s;   // free: receives V(j+1)
-    if (j + 2 < ntiles) tile_to_lds<D, kBC, kThreads>(rk, (j + 2) * kBC, k_this, tid);
-    if (j + 1 < ntiles) tile_to_lds<D, kBC, kThreads>(rv, (j + 1) * kBC, v_next, tid);
+    if (j + 2 < ntiles) copy(mk, (j + 2) * kBC, k_this);
+    if (j + 1 < ntiles) copy(mv, (j + 1) * kBC, v_next);
     const int kv0 = j * kBC;
     if (j < wave_tiles) {
       // Accumulator element (kb, r) is key kv0 + 32kb + 8(r/4) + 4g + (r%4) for query qi.

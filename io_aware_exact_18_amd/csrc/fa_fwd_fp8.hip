@@ -41,24 +41,6 @@ __device__ inline int swz8(int r) { return (((r >> 1) & 3) << 1) | ((r >> 3) & 1
 // Rows 32kb + i of the A operand hold K row 32kb + perm(i): bits 2 and 3 of i swapped.
 __device__ inline int perm23(int i) { return (i & ~0xC) | ((i >> 1) & 4) | ((i << 1) & 8); }
 
-template <int ROWS>
-__device__ inline void tile8_to_lds(__amdgpu_buffer_rsrc_t r, int row0, uint8_t* lds, int tid) {
-  constexpr int CPR = kRowBytes / 16;
-  constexpr int CHUNKS = ROWS * CPR;
-  static_assert(CHUNKS % kThreads == 0, "tile must split evenly");
-  const int wave = tid >> 6, lane = tid & 63;
-#pragma unroll
-  for (int i = 0; i < CHUNKS / kThreads; ++i) {
-    const int blk = i * (kThreads / 64) + wave;
-    const int slot = blk * 64 + lane;
-    const int row = slot / CPR, pc = slot % CPR;
-    const int c = pc ^ swz8(row);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        r, (__attribute__((address_space(3))) void*)(lds + blk * 1024), 16,
-        (uint32_t)((row0 + row) * kRowBytes + 16 * c), 0, 0, 0);
-  }
-}
-
 __device__ inline f32x16 mfma_f8(i32x8 a, i32x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
@@ -87,7 +69,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_fp8_kernel(
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = wave_index(tid);
   const int g = lane >> 5;
   const int lc = lane & 31;
 
@@ -102,8 +84,9 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_fp8_kernel(
   const size_t head = (size_t)bh * N * kD;
   const uint32_t head_bytes = (uint32_t)N * kRowBytes;
   const auto rq = make_rsrc(Q + head, head_bytes);
-  const auto rk = make_rsrc(K + head, head_bytes);
-  const auto rv = make_rsrc(V + head, head_bytes);
+  const auto mk = make_rsrc(K + head, head_bytes);
+  const auto mv = make_rsrc(V + head, head_bytes);
+  const TileCopy<kRowBytes, kBC, kThreads> copy(tid, [](int r) { return swz8(r); });
 
   // Qᵀ operand (B): this lane's query, k-step s covers d = 64s + 32g .. +31.
   i32x8 qf[2];
@@ -141,9 +124,9 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_fp8_kernel(
   const int ntiles = (kv_end + kBC - 1) / kBC;
   const int wave_tiles = CAUSAL ? min(ntiles, (qw + 31) / kBC + 1) : ntiles;
 
-  tile8_to_lds<kBC>(rk, 0, k0s, tid);
-  if (ntiles > 1) tile8_to_lds<kBC>(rk, kBC, k1s, tid);
-  tile8_to_lds<kBC>(rv, 0, v0s, tid);
+  copy(mk, 0, k0s);
+  if (ntiles > 1) copy(mk, kBC, k1s);
+  copy(mv, 0, v0s);
   wait_vmem_all();
   __syncthreads();
 
@@ -184,8 +167,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_fp8_kernel(
     uint8_t* const k_next = P ? k0s : k1s;
     uint8_t* const v_this = P ? v1s : v0s;
     uint8_t* const v_next = P ? v0s : v1s;
-    if (j + 2 < ntiles) tile8_to_lds<kBC>(rk, (j + 2) * kBC, k_this, tid);
-    if (j + 1 < ntiles) tile8_to_lds<kBC>(rv, (j + 1) * kBC, v_next, tid);
+    if (j + 2 < ntiles) copy(mk, (j + 2) * kBC, k_this);
+    if (j + 1 < ntiles) copy(mv, (j + 1) * kBC, v_next);
     const int kv0 = j * kBC;
     if (j < wave_tiles) {
       // Accumulator element (kb, r), r = 4q + t, is key kv0 + 32kb + 16(q/2) + 8g + 4(q%2) + t.
