@@ -15,10 +15,14 @@
 //   * The probabilities leave the accumulator as bf16 and feed Oᵀ += Vᵀ Pᵀ directly as the B
 //     operand; V is read from its row-major LDS tile with ds_read_b64_tr_b16, whose key order matches
 //     the accumulator's row order, so P never goes through LDS.
-//   * Software pipeline: K tiles are staged one tile ahead of V tiles, so while the vector units run
-//     the softmax of tile j the matrix cores already compute the scores of tile j + 1 (the overlap of
-//     matrix products with the softmax that "Anatomy ...", section "What changed between
-//     FlashAttention 1, 2, and 3?", credits for FA3's speed, done here within one wave).
+//   * Software pipeline: K tiles are staged one tile ahead of V tiles and each tile runs in two
+//     phases that pair matrix-core and vector work of different tiles: (A) the scores of tile j + 1
+//     with the exponentials of tile j, (B) Oᵀ += Vᵀ Pᵀ of tile j with the row sum of tile j and the
+//     row maximum of tile j + 1 (the overlap of matrix products with the softmax that "Anatomy ...",
+//     section "What changed between FlashAttention 1, 2, and 3?", credits for FA3's speed, done here
+//     within one wave).
+//   * The exponentials use a reference maximum that moves only when a row's maximum exceeds it by
+//     more than 2^8 (kSlack), so the accumulator rescale of the online softmax runs on few tiles.
 //   * The softmax runs in base 2 with scale·log2(e) folded into one FMA; normalisation by the row sum
 //     is deferred to the end (fewer non-matmul operations, same section).  LSE is converted back to
 //     natural log on output.
@@ -35,6 +39,19 @@ namespace {
 constexpr int kBR = 128;   // queries per workgroup
 constexpr int kBC = 64;    // keys per tile
 constexpr int kThreads = 256;
+// The exponentials use a per-row reference maximum that is raised only when some row of the wave
+// sees a score more than kSlack (base-2 units) above its reference; until then p ≤ 2^kSlack, which
+// bf16 P and the fp32 sums hold exactly as well as p ≤ 1.  Output and row sum share the reference,
+// so the result is the same softmax; the rescale of the accumulators becomes rare instead of
+// happening on most tiles (with 32 rows per wave, some row's running maximum rises on most tiles).
+constexpr float kSlack = 8.f;
+
+// Compile-time selection between two objects (the score tiles of the two tile parities).
+template <int P, class T>
+__device__ inline T& pick(T& a, T& b) {
+  if constexpr (P != 0) return b;
+  else return a;
+}
 
 
 // Sᵀ = K Qᵀ for one 64-key tile: acc[kb] element r is key 32kb + 8(r/4) + 4g + (r%4) of the tile,
@@ -110,11 +127,22 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
   wait_vmem_all();
   __syncthreads();
 
-  f32x16 s_cur[2], s_nxt[2];
-  scores_tile<D>((const char*)k0s, fo, qf, s_cur);
+  // Score tiles of the even and odd tiles: tile j's scores are in sa when j is even, sb when odd.
+  f32x16 sa[2], sb[2];
+  // Row maximum of a score tile (raw scores; both half-waves get the same value).
+  auto rowmax = [](const f32x16(&s)[2]) {
+    float mx = fmaxf(s[0][0], s[1][0]);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+    return halves_max(mx);
+  };
+  scores_tile<D>((const char*)k0s, fo, qf, sa);
+  float mx = rowmax(sa);  // row maximum of the current tile's (unmasked) scores
   __syncthreads();  // every wave is done with k[0] before K(2) overwrites it
 
-  float m = -INFINITY;  // running max of the base-2 scaled scores
+  float m = -INFINITY;  // reference maximum of the base-2 scaled scores (see kSlack)
   float l = 0.f;        // running sum of 2^(t - m) over this lane's keys (half of the row)
   f32x16 oacc[DB];
 #pragma unroll
@@ -126,6 +154,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
   // base plus an immediate.  Buffers on entry: k[P^1] = K(j+1), v[P] = V(j); k[P], v[P^1] are free.
   auto tile = [&](auto parity, int j) {
     constexpr int P = decltype(parity)::value;
+    f32x16(&s_cur)[2] = pick<P>(sa, sb);  // scores of tile j
+    f32x16(&s_nxt)[2] = pick<P>(sb, sa);  // receives the scores of tile j + 1
     bf16* const k_this = P ? k1s : k0s;   // free: receives K(j+2)
     bf16* const k_next = P ? k0s : k1s;   // holds K(j+1)
     bf16* const v_this = P ? v1s : v0s;   // holds V(j)
@@ -134,9 +164,9 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     if (j + 1 < ntiles) copy(mv, (j + 1) * kBC, v_next);
     const int kv0 = j * kBC;
     if (j < wave_tiles) {
-      // Accumulator element (kb, r) is key kv0 + 32kb + 8(r/4) + 4g + (r%4) for query qi.
-      const bool need_mask = (kv0 + kBC > N) || (CAUSAL && kv0 + kBC - 1 > qw);
-      if (need_mask) {
+      // Accumulator element (kb, r) is key kv0 + 32kb + 8(r/4) + 4g + (r%4) for query qi.  Diagonal
+      // and ragged tiles are masked here and their maximum is taken again.
+      if ((kv0 + kBC > N) || (CAUSAL && kv0 + kBC - 1 > qw)) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -144,50 +174,46 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
             const int key = kv0 + 32 * kb + 8 * (r >> 2) + 4 * g + (r & 3);
             if (key >= N || (CAUSAL && key > qi)) s_cur[kb][r] = -INFINITY;
           }
+        mx = rowmax(s_cur);
       }
-      float mx = fmaxf(s_cur[0][0], s_cur[1][0]);
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s_cur[kb][r]);
-      mx = halves_max(mx);
-      const float m_new = fmaxf(m, mx * scale_log2);
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      // Rescale the output accumulator only when some row's maximum moved (alpha != 1 somewhere in
-      // the wave); once the maxima settle, most tiles skip these multiplies.
-      if (!wave_all(m_new == m)) {
-        const float alpha = exp2_fast(m - m_use);
+      const float mt = mx * scale_log2;
+      // Raise the reference (and rescale) only when some row's tile maximum exceeds it by more than
+      // kSlack; a row still without any unmasked key keeps m = -inf.
+      if (!wave_all(mt <= m + kSlack)) {
+        const float m_new = fmaxf(m, mt);
+        const float alpha = exp2_fast(m - (m_new == -INFINITY ? 0.f : m_new));
         l *= alpha;
 #pragma unroll
         for (int b = 0; b < DB; ++b)
 #pragma unroll
           for (int r = 0; r < 16; ++r) oacc[b][r] *= alpha;
+        m = m_new;
       }
-      m = m_new;
+      const float m_use = (m == -INFINITY) ? 0.f : m;
 
-      // One branch-free block: the scores of tile j + 1 on the matrix cores (on a wave's last tile
-      // they read a stale buffer and are discarded) and the exponentials of tile j on the vector
-      // units; the group barriers at its end interleave the two streams.
+      // Two branch-free phases, each pairing matrix-core work with independent vector work so that
+      // one wave keeps both units busy (the group barriers set the interleave).
+      // Phase A: scores of tile j + 1 (on a wave's last tile they read a stale buffer and are
+      // discarded) with the probabilities of tile j, kept in place in s_cur and as the bf16 Pᵀ
+      // operand: k-step ks (16 keys) takes registers 8(ks%2) .. +7 of key block ks/2, i.e. keys
+      // 16ks + 8(e/4) + 4g + (e%4) — the order the transposed V reads below produce.
       scores_tile<D>((const char*)k_next, fo, qf, s_nxt);
-      float rs[4] = {0.f, 0.f, 0.f, 0.f};  // four partial sums: shorter dependency chains
       bf16x8 pf[4];
-      // Pᵀ operand for k-step ks (16 keys): slots e = registers 8(ks%2) + e of key block ks/2, i.e.
-      // keys 16ks + 8(e/4) + 4g + (e%4) — the order the transposed V reads below produce.
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const float p = exp2_fast(fmaf(s_cur[ks >> 1][8 * (ks & 1) + e], scale_log2, -m_use));
-          rs[e & 3] += p;
+          s_cur[ks >> 1][8 * (ks & 1) + e] = p;
           pf[ks][e] = (__bf16)p;
         }
-      l += (rs[0] + rs[1]) + (rs[2] + rs[3]);
 #pragma unroll
       for (int i = 0; i < 2 * KSTEPS; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one matrix-core op
-        __builtin_amdgcn_sched_group_barrier(0x002, 7, 0);  // seven vector ALU ops
+        __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // three vector ALU ops
       }
-
+      __builtin_amdgcn_sched_barrier(0);
+      // Phase B: Oᵀ += Vᵀ Pᵀ with the row sum of tile j and the row maximum of tile j + 1.
       const char* vlds = (const char*)v_this;
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
@@ -197,8 +223,18 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
 #pragma unroll
         for (int b = 0; b < DB; ++b) oacc[b] = mfma_32x32x16(vf[b], pf[ks], oacc[b]);
       }
+      float rs[4] = {s_cur[0][0], s_cur[0][1], s_cur[0][2], s_cur[0][3]};  // four partial sums
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) s_cur[kb] = s_nxt[kb];
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = (kb == 0 ? 4 : 0); r < 16; ++r) rs[r & 3] += s_cur[kb][r];
+      l += (rs[0] + rs[1]) + (rs[2] + rs[3]);
+      mx = rowmax(s_nxt);
+#pragma unroll
+      for (int i = 0; i < 2 * KSTEPS; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+      }
     }
     wait_vmem_all();
     __syncthreads();

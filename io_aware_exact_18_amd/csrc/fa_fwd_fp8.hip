@@ -7,10 +7,11 @@
 //
 //   * Sᵀ = K Qᵀ on v_mfma_f32_32x32x64_f8f6f4 (fp32 accumulation; products of e4m3 values are exact).
 //     The descales and scale·log2(e) fold into the one FMA that forms the exponent.
-//   * P = 2^(s − m + 8) ∈ [0, 256] is rounded to e4m3 (v_cvt_pk_fp8_f32: round-to-nearest-even,
-//     saturating at 448) and Oᵀ += Vᵀ Pᵀ runs on the same fp8 matrix core.  The factor 2^8 (free: it
-//     is part of the FMA's constant) keeps small probabilities out of e4m3's subnormal range; it
-//     cancels in O = Σ P V / Σ P and is removed from LSE.  The row sum l is formed by one more
+//   * P = 2^(s − m + 6) ∈ [0, 256] is rounded to e4m3 (v_cvt_pk_fp8_f32: round-to-nearest-even,
+//     saturating at 448) and Oᵀ += Vᵀ Pᵀ runs on the same fp8 matrix core.  m is a reference maximum
+//     that trails the running maximum by at most 2, so P ≤ 2^8; the factor 2^6 (free: it is part of
+//     the FMA's constant) keeps small probabilities out of e4m3's subnormal range; both cancel in
+//     O = Σ P V / Σ P and are removed from LSE.  The row sum l is formed by one more
 //     matrix-core op against an all-ones operand, so it sums exactly the rounded P values that enter
 //     P·V.
 //   * Key order: each wave loads K rows into the A operand with bits 2 and 3 of the row index swapped,
@@ -32,7 +33,17 @@ constexpr int kBR = 128;
 constexpr int kBC = 64;
 constexpr int kThreads = 256;
 constexpr int kRowBytes = kD;  // one e4m3 byte per element
-constexpr float kPExp = 8.f;   // P is formed as 2^(s − m + kPExp)
+// P is formed as 2^(s·c − m + kPExp) against a per-row reference maximum m that is raised only when
+// some row of the wave sees a score more than kSlack above it, so P ≤ 2^(kPExp + kSlack) = 256 fits
+// e4m3 (largest finite 448) and the accumulators are rescaled on few tiles instead of most.
+constexpr float kPExp = 6.f;
+constexpr float kSlack = 2.f;
+
+template <int P, class T>
+__device__ inline T& pick(T& a, T& b) {
+  if constexpr (P != 0) return b;
+  else return a;
+}
 
 // Swizzle of 16-byte chunks within a 128-byte fp8 row (64 banks; two rows per bank period): keeps
 // 16-lane row reads and 32-lane 8-byte transposed reads conflict-free.
@@ -146,8 +157,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_fp8_kernel(
     }
   };
 
-  f32x16 s_cur[2], s_nxt[2];
-  scores(k0s, s_cur);
+  f32x16 sa[2], sb[2];  // scores of the even / odd tiles
+  scores(k0s, sa);
   __syncthreads();
 
   float m = -INFINITY;
@@ -163,6 +174,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_fp8_kernel(
 
   auto tile = [&](auto parity, int j) {
     constexpr int P = decltype(parity)::value;
+    f32x16(&s_cur)[2] = pick<P>(sa, sb);  // scores of tile j
+    f32x16(&s_nxt)[2] = pick<P>(sb, sa);  // receives the scores of tile j + 1
     uint8_t* const k_this = P ? k1s : k0s;
     uint8_t* const k_next = P ? k0s : k1s;
     uint8_t* const v_this = P ? v1s : v0s;
@@ -189,19 +202,19 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_fp8_kernel(
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s_cur[kb][r]);
       mx = halves_max(mx);
-      const float m_new = fmaxf(m, mx * c_log2);
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      const float m_off = m_use - kPExp;  // exponent offset: P = 2^(s·c − m + 8)
-      if (!wave_all(m_new == m)) {
-        const float alpha = exp2_fast(m - m_use);
+      const float mt = mx * c_log2;
+      if (!wave_all(mt <= m + kSlack)) {  // raise the reference; a row without keys keeps -inf
+        const float m_new = fmaxf(m, mt);
+        const float alpha = exp2_fast(m - (m_new == -INFINITY ? 0.f : m_new));
 #pragma unroll
         for (int b = 0; b < 4; ++b)
 #pragma unroll
           for (int r = 0; r < 16; ++r) oacc[b][r] *= alpha;
 #pragma unroll
         for (int r = 0; r < 16; ++r) lacc[r] *= alpha;
+        m = m_new;
       }
-      m = m_new;
+      const float m_off = (m == -INFINITY ? 0.f : m) - kPExp;  // P = 2^(s·c − m + kPExp)
 
       scores(k_next, s_nxt);  // next tile's scores; discarded on the wave's last tile
       // Pᵀ operand (B): byte e of the 8 registers is P for accumulator element (e/16, e%16), i.e.
@@ -235,8 +248,6 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_fp8_kernel(
         oacc[db] = mfma_f8(vf, pf, oacc[db]);
       }
       lacc = mfma_f8(ones, pf, lacc);  // every row: Σ over the tile's keys of the rounded P
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) s_cur[kb] = s_nxt[kb];
     }
     wait_vmem_all();
     __syncthreads();
