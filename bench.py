@@ -36,9 +36,12 @@ def log(*a):
 
 
 def source_sha(name):
-    path = os.path.join(ROOT, "io_aware_exact_18_amd", "csrc", name)
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """sha256 prefix over a kernel's source file and the device headers every kernel includes."""
+    h = hashlib.sha256()
+    for part in (name, "fa_common.h", "fa_launch.h"):
+        with open(os.path.join(ROOT, "io_aware_exact_18_amd", "csrc", part), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic(kernel, src):
