@@ -197,6 +197,9 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
       // discarded) with the probabilities of tile j, kept in place in s_cur and as the bf16 Pᵀ
       // operand: k-step ks (16 keys) takes registers 8(ks%2) .. +7 of key block ks/2, i.e. keys
       // 16ks + 8(e/4) + 4g + (e%4) — the order the transposed V reads below produce.
+      // Phase A runs at raised wave priority: when both waves of a SIMD can issue, the one in its
+      // score/exponential phase goes first (measured 2% faster than equal priorities).
+      __builtin_amdgcn_s_setprio(1);
       scores_tile<D>((const char*)k_next, fo, qf, s_nxt);
       bf16x8 pf[4];
 #pragma unroll
@@ -213,6 +216,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
         __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // three vector ALU ops
       }
       __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_setprio(0);
       // Phase B: Oᵀ += Vᵀ Pᵀ with the row sum of tile j and the row maximum of tile j + 1.
       const char* vlds = (const char*)v_this;
 #pragma unroll
