@@ -93,6 +93,111 @@ def cpu_baseline(w, inp, budget_s):
     }
 
 
+def sclk_sysfs_path(torch):
+    """The pp_dpm_sclk file of the device torch calls cuda:0, found by its PCI address, or None."""
+    import glob
+    pr = torch.cuda.get_device_properties(0)
+    want = f"{pr.pci_domain_id:04x}:{pr.pci_bus_id:02x}:{pr.pci_device_id:02x}."
+    for card in glob.glob("/sys/class/drm/card*/device"):
+        try:
+            if os.path.basename(os.path.realpath(card)).startswith(want):
+                path = os.path.join(card, "pp_dpm_sclk")
+                return path if os.access(path, os.R_OK) else None
+        except OSError:
+            continue
+    return None
+
+
+def sample_sclk(path, busy, seconds=1.0, period=0.01):
+    """Mean shader clock (MHz) read from the driver's current-level line of pp_dpm_sclk while
+    `busy()` keeps the GPU loaded for about `seconds`; None if the file cannot be read."""
+    import threading
+    samples, stop = [], threading.Event()
+
+    def reader():
+        while not stop.is_set():
+            try:
+                with open(path) as f:
+                    for line in f:
+                        if "*" in line:
+                            mhz = "".join(ch for ch in line.split(":", 1)[1] if ch.isdigit())
+                            if mhz:
+                                samples.append(int(mhz))
+            except OSError:
+                return
+            time.sleep(period)
+
+    th = threading.Thread(target=reader, daemon=True)
+    th.start()
+    t_end = time.perf_counter() + seconds
+    while time.perf_counter() < t_end:
+        busy()
+    stop.set()
+    th.join()
+    if not samples:
+        return None
+    return {"mean_mhz": sum(samples) / len(samples), "min_mhz": min(samples),
+            "max_mhz": max(samples), "samples": len(samples), "source": path}
+
+
+def device_block(fa, torch, busy):
+    """Device facts reported beside the measurement: the bf16 peak recomputed from the device's
+    compute units × peak clock × 4096 FLOP/clk/CU, and the shader clock seen under this load."""
+    cus, khz = fa.device_info(0)
+    path = sclk_sysfs_path(torch)
+    return {
+        "name": torch.cuda.get_device_properties(0).name,
+        "arch": torch.cuda.get_device_properties(0).gcnArchName,
+        "compute_units": cus,
+        "peak_clock_mhz": khz / 1e3,
+        "bf16_peak_from_device_tflops": cus * khz * 1e3 * 4096 / 1e12,
+        "sclk_under_load": sample_sclk(path, busy) if path else None,
+    }
+
+
+def cpu_full_runs(workloads):
+    """The oracle over every head of the two small workloads (forward, and backward where the
+    workload has one), timed in full."""
+    import oracle
+    out = {}
+    for name in ("fwd_small", "d64_2k"):
+        w = workloads.WORKLOADS[name]
+        B, H, N, d = w.shape()
+        inp = workloads.make_inputs(name)
+        flat = {k: inp[k].reshape(B * H, N, d) for k in inp}
+        t0 = time.perf_counter()
+        for h in range(B * H):
+            q, k, v = (flat[x][h].double().numpy() for x in ("q", "k", "v"))
+            oracle.attention_head_fwd64(q, k, v, w.causal, w.scale)
+            if w.backward:
+                oracle.attention_head_bwd64(q, k, v, flat["do"][h].double().numpy(), w.causal,
+                                            w.scale)
+        t = time.perf_counter() - t0
+        flops = w.fwd_flops() + (w.bwd_flops() if w.backward else 0)
+        out[name] = {"seconds": t, "heads": B * H, "tflops": flops / t / 1e12,
+                     "passes": "forward+backward" if w.backward else "forward"}
+    return out
+
+
+def traffic_sweep(fa, torch, steps):
+    """Forward at N = 1k..16k (B=1, H=32, d=128, causal), `steps` launches each, for HBM byte
+    counters: measured bytes should grow linearly in N while S and P, had they been materialised in
+    bf16 (written and read once each), would grow as N²."""
+    B, H, d = 1, 32, 128
+    g = torch.Generator().manual_seed(77)
+    for N in (1024, 2048, 4096, 8192, 16384):
+        q, k, v = (torch.randn(B, H, N, d, generator=g).to(torch.bfloat16).to("cuda:0")
+                   for _ in range(3))
+        for _ in range(steps):
+            o, lse = fa.fwd(q, k, v, True, 1.0 / math.sqrt(d))
+        torch.cuda.synchronize()
+        print(json.dumps({"N": N, "B": B, "H": H, "d": d, "launches": steps,
+                          "grid_workgroups": B * H * ((N + 127) // 128),
+                          "algorithmic_bytes": 4 * B * H * N * d * 2 + B * H * N * 4,
+                          "materialised_s_p_bytes": 4 * B * H * N * N * 2}), flush=True)
+        del q, k, v, o, lse
+
+
 def fp8_forward(fa, workloads, lib, steps, warmup):
     """Secondary measurement: the FP8 forward on its workload (fp8_8k), timed with events."""
     import torch
@@ -139,6 +244,9 @@ def main():
                     help="seconds of oracle work for the cpu_baseline leg (0 skips it)")
     ap.add_argument("--no-fp8", action="store_true",
                     help="skip the secondary FP8 forward measurement (fp8_8k workload)")
+    ap.add_argument("--traffic-sweep", action="store_true",
+                    help="instead of the bench, run the forward at N = 1k..16k (B=1, H=32, d=128, "
+                         "causal) `--steps` times each, for HBM byte counters")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of the bench, run a plain device copy of MIB MiB `--steps` times "
                          "(the reference kernel for scaling HBM byte counters)")
@@ -164,6 +272,9 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes": n, "copies": args.steps}))
+        return
+    if args.traffic_sweep:
+        traffic_sweep(fa, torch, args.steps)
         return
     w = workloads.WORKLOADS[args.workload]
     if w.fp8 or not w.backward:
@@ -226,10 +337,15 @@ def main():
     ms_per_step = elapsed * 1e3 / args.steps
     log(f"[bench] timed {args.steps} steps: {ms_per_step:.3f} ms/step")
 
+    def durations(a, b):
+        return sorted(e[a].elapsed_time(e[b]) for e in events)
+
     def avg(a, b):
-        return sum(e[a].elapsed_time(e[b]) for e in events) / len(events)
+        return sum(durations(a, b)) / len(events)
 
     fwd_ms, pre_ms, dkdv_ms, dq_ms = avg(0, 1), avg(1, 2), avg(2, 3), avg(3, 4)
+    spans = {"fwd_bf16_kernel": (0, 1), "bwd_pre_kernel": (1, 2), "bwd_dkdv_kernel": (2, 3),
+             "bwd_dq_kernel": (3, 4)}
     fwd_f, bwd_f = w.fwd_flops(), w.bwd_flops()
     value = (fwd_f + bwd_f) / (ms_per_step * 1e-3) / 1e12
 
@@ -246,7 +362,10 @@ def main():
         "bwd_dq_kernel": {"ms": dq_ms, "flops": bwd_f * 1 / 5, "src": "fa_bwd.hip"},
         "bwd_pre_kernel": {"ms": pre_ms, "src": "fa_bwd.hip"},
     }
-    for kk in kernels.values():
+    for name, kk in kernels.items():
+        dd = durations(*spans[name])
+        kk["median_ms"] = dd[len(dd) // 2] if len(dd) % 2 else (dd[len(dd) // 2 - 1] + dd[len(dd) // 2]) / 2
+        kk["min_ms"] = dd[0]
         if "flops" in kk:
             kk["tflops"] = kk["flops"] / (kk["ms"] * 1e-3) / 1e12
     dom = max(("fwd_bf16_kernel", "bwd_dkdv_kernel", "bwd_dq_kernel"),
@@ -263,6 +382,9 @@ def main():
         "launch_ms": dom_k["ms"],
     }
 
+    log("[bench] sampling the shader clock under the same load for ~1 s")
+    device = device_block(fa, torch, lambda: (step(), torch.cuda.synchronize(dev)))
+
     secondary = {}
     if not args.no_fp8:
         secondary["fp8_8k_fwd"] = fp8_forward(fa, workloads, lib, args.steps, args.warmup)
@@ -272,6 +394,8 @@ def main():
         log(f"[bench] timing the CPU oracle for ~{args.cpu_budget:.0f} s")
         cpu = cpu_baseline(w, inp, args.cpu_budget)
         log(f"[bench] oracle: {cpu['value']:.4f} TFLOP/s on {cpu['cores']} threads")
+        log("[bench] timing the oracle over the two small workloads in full")
+        cpu["full_runs"] = cpu_full_runs(workloads)
 
     out = {
         "metric": METRIC,
@@ -295,6 +419,7 @@ def main():
         "bwd_tflops": bwd_f / ((pre_ms + dkdv_ms + dq_ms) * 1e-3) / 1e12,
         "kernels": {n: {k2: v2 for k2, v2 in kk.items() if k2 != "src"} for n, kk in kernels.items()},
         "roofline": roofline,
+        "device": device,
         "secondary": secondary,
         "cpu_baseline": cpu,
     }

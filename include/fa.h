@@ -117,6 +117,13 @@ fa_status fa_bwd_dq(const void* q, const void* k, const void* v, const float* ls
 /* A static, human-readable name for a status code (never NULL). */
 const char* fa_status_str(fa_status status);
 
+/* Device facts for pricing measurements against the hardware: the number of compute units and the
+ * peak shader clock (kHz) of HIP device `device`, as the HIP runtime reports them
+ * (hipDeviceGetAttribute).  Writes both outputs and returns FA_OK; FA_ERR_NULL if an output pointer
+ * is NULL; FA_ERR_LAUNCH if the runtime query fails (no such device).  Allocates nothing and
+ * launches nothing.  Not part of the attention computation. */
+fa_status fa_device_info(int device, int* compute_units, int* peak_clock_khz);
+
 #ifdef __cplusplus
 }
 #endif

@@ -12,6 +12,7 @@ Entry points (same names as the C ABI, without the ``fa_`` prefix):
   bwd_workspace_bytes(B, H, N, d) -> int
   bwd_preprocess / bwd_dkdv / bwd_dq — the three phases fa_bwd runs, for timing them apart
   status_str(code) -> str
+  device_info(device=0) -> (compute units, peak clock kHz), for pricing measurements
 """
 
 import ctypes
@@ -21,7 +22,7 @@ import os
 import torch
 
 __all__ = ["fwd", "fwd_fp8", "bwd", "bwd_workspace_bytes", "bwd_preprocess", "bwd_dkdv",
-           "bwd_dq", "status_str", "FaError", "library", "LIB_PATH"]
+           "bwd_dq", "status_str", "device_info", "FaError", "library", "LIB_PATH"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
 
@@ -65,8 +66,17 @@ def library():
         lib.fa_bwd_dq.restype = i
         lib.fa_status_str.argtypes = [i]
         lib.fa_status_str.restype = ctypes.c_char_p
+        lib.fa_device_info.argtypes = [i, vp, vp]
+        lib.fa_device_info.restype = i
         _lib = lib
     return _lib
+
+
+def device_info(device=0):
+    """(compute units, peak shader clock in kHz) of a HIP device, from fa_device_info."""
+    cus, khz = ctypes.c_int(0), ctypes.c_int(0)
+    _check("fa_device_info", library().fa_device_info(int(device), ctypes.byref(cus), ctypes.byref(khz)))
+    return cus.value, khz.value
 
 
 def status_str(code):

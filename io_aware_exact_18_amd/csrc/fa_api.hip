@@ -30,6 +30,17 @@ bool good_scale(float s) { return isfinite(s) && s > 0.f; }
 
 extern "C" {
 
+fa_status fa_device_info(int device, int* compute_units, int* peak_clock_khz) {
+  if (compute_units == nullptr || peak_clock_khz == nullptr) return FA_ERR_NULL;
+  int cus = 0, khz = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess ||
+      hipDeviceGetAttribute(&khz, hipDeviceAttributeClockRate, device) != hipSuccess)
+    return FA_ERR_LAUNCH;
+  *compute_units = cus;
+  *peak_clock_khz = khz;
+  return FA_OK;
+}
+
 const char* fa_status_str(fa_status status) {
   switch (status) {
     case FA_OK: return "FA_OK";

@@ -32,6 +32,7 @@ def lib():
     lib.fa_bwd_dq.argtypes = [vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, f, vp]
     lib.fa_status_str.argtypes = [i]
     lib.fa_status_str.restype = ctypes.c_char_p
+    lib.fa_device_info.argtypes = [i, vp, vp]
     return lib
 
 
@@ -39,9 +40,15 @@ def test_exports_match_header(lib):
     text = open(HEADER).read()
     declared = set(re.findall(r"^\s*(?:fa_status|size_t|const char\*)\s+(fa_\w+)\s*\(", text, re.M))
     assert declared == {"fa_fwd", "fa_fwd_fp8", "fa_bwd_workspace_bytes", "fa_bwd", "fa_status_str",
-                        "fa_bwd_preprocess", "fa_bwd_dkdv", "fa_bwd_dq"}
+                        "fa_bwd_preprocess", "fa_bwd_dkdv", "fa_bwd_dq", "fa_device_info"}
     for name in declared:
         assert hasattr(lib, name), name
+
+
+def test_device_info_null_outputs(lib):
+    x = ctypes.c_int(0)
+    assert lib.fa_device_info(0, None, ctypes.byref(x)) == NULL
+    assert lib.fa_device_info(0, ctypes.byref(x), None) == NULL
 
 
 def test_status_strings(lib):
