@@ -22,6 +22,16 @@ What it computes, and where the pages define it:
   rescale of the accumulated denominator and output by exp(m_old − m_new) whenever a new tile raises m.
 * Causal masking (key j may be used by query i only when j ≤ i) is not on the pages; it is the plain
   reading used for the causal workloads.
+* Decoding against a key/value cache (the inference use the pages pair FlashAttention with: glossary
+  entry "flash attention", paragraph on long-context training and serving; "FlashAttention: where it
+  matters", section "Where It Matters", long-context inference and speculative decoding): a few new
+  queries attend over Nk cached keys.  The queries are the last Nq positions of the sequence, so with
+  the causal mask query i (0-based) sits at position q_offset + i with q_offset = Nk − Nq and may use
+  key j when j ≤ q_offset + i.  ``q_offset`` is a parameter of the score functions (0 reproduces the
+  square case).
+* Splitting the keys into chunks, attending to each chunk on its own and combining the per-chunk
+  results is the online-softmax recurrence applied to whole chunks: per row, with partial results
+  (O_s, LSE_s), LSE = log Σ_s exp(LSE_s) and O = Σ_s exp(LSE_s − LSE) · O_s (``merge_partials64``).
 
 Layout: every tensor argument is a numpy array [B, H, N, d] (LSE: [B, H, N]); arithmetic is float64.
 Per-head ("_head") functions take 2-D [N, d] arrays.
@@ -42,6 +52,8 @@ __all__ = [
     "online_attention_head64",
     "brute_attention_head",
     "brute_attention_head_bwd",
+    "merge_partials64",
+    "split_attention_head64",
 ]
 
 
@@ -49,10 +61,11 @@ def _as64(x):
     return np.asarray(x, dtype=np.float64)
 
 
-def scores_head64(q, k, causal, scale):
+def scores_head64(q, k, causal, scale, q_offset=0):
     """Scaled scores S = scale · Q Kᵀ for one head, with masked entries set to −inf.
 
-    Masking: causal keeps key j for query i only when j ≤ i (same sequence for queries and keys).
+    Masking: causal keeps key j for query i only when j ≤ q_offset + i, query i being at position
+    q_offset + i of the key sequence (0 for the square case, Nk − Nq for decoding).
     """
     q = _as64(q)
     k = _as64(k)
@@ -61,7 +74,7 @@ def scores_head64(q, k, causal, scale):
         n_q, n_k = s.shape
         i = np.arange(n_q)[:, None]
         j = np.arange(n_k)[None, :]
-        s = np.where(j > i, -np.inf, s)
+        s = np.where(j > q_offset + i, -np.inf, s)
     return s
 
 
@@ -77,9 +90,12 @@ def probabilities_head64(s):
     return p, m, l
 
 
-def attention_head_fwd64(q, k, v, causal, scale):
-    """Forward for one head: O = P V and LSE_i = m_i + ln l_i (natural log, of the scaled scores)."""
-    s = scores_head64(q, k, causal, scale)
+def attention_head_fwd64(q, k, v, causal, scale, q_offset=0):
+    """Forward for one head: O = P V and LSE_i = m_i + ln l_i (natural log, of the scaled scores).
+
+    ``q_offset``: position of query 0 in the key sequence for the causal mask (see scores_head64).
+    """
+    s = scores_head64(q, k, causal, scale, q_offset)
     p, m, l = probabilities_head64(s)
     o = p @ _as64(v)
     lse = m + np.log(l)
@@ -211,11 +227,11 @@ def online_attention_head64(q, k, v, causal, scale, tile_r, tile_c):
     return o, lse
 
 
-def brute_attention_head(q, k, v, causal, scale):
+def brute_attention_head(q, k, v, causal, scale, q_offset=0):
     """Forward for one head with plain Python loops and the math module (tiny inputs only).
 
-    Written independently of the numpy functions above, entry by entry from the definition.
-    Returns (o, lse) as nested lists.
+    Written independently of the numpy functions above, entry by entry from the definition; with the
+    causal mask query i may use key j when j ≤ q_offset + i.  Returns (o, lse) as nested lists.
     """
     n_q, n_k = len(q), len(k)
     d = len(q[0])
@@ -223,7 +239,7 @@ def brute_attention_head(q, k, v, causal, scale):
     o = []
     lse = []
     for i in range(n_q):
-        allowed = [j for j in range(n_k) if (not causal) or j <= i]
+        allowed = [j for j in range(n_k) if (not causal) or j <= q_offset + i]
         s = {}
         for j in allowed:
             acc = 0.0
@@ -272,3 +288,44 @@ def brute_attention_head_bwd(q, k, v, do, causal, scale):
     dk = [[scale * sum(ds[i][j] * float(q[i][t]) for i in range(n_q)) for t in range(d)]
           for j in range(n_k)]
     return dq, dk, dv
+
+
+def merge_partials64(parts):
+    """Combine per-chunk attention results of the same query rows into the result over all chunks.
+
+    ``parts``: list of (O_s [Nq, d], LSE_s [Nq]) where chunk s attended to its own keys only (a row with
+    no usable key in a chunk has LSE_s = −inf and any finite O_s).  With M = max_s LSE_s,
+      LSE = M + ln Σ_s exp(LSE_s − M),   O = Σ_s exp(LSE_s − LSE) · O_s,
+    i.e. each chunk's output weighted by its share of the row's total softmax mass.
+    """
+    lses = np.stack([_as64(l) for _, l in parts])          # [S, Nq]
+    outs = np.stack([_as64(o) for o, _ in parts])          # [S, Nq, d]
+    mx = np.max(lses, axis=0)
+    w = np.exp(lses - mx[None, :])                          # exp(−inf) = 0 drops empty chunks
+    tot = np.sum(w, axis=0)
+    lse = mx + np.log(tot)
+    outs = np.where(np.isfinite(lses)[:, :, None], outs, 0.0)
+    o = np.sum((w / tot[None, :])[:, :, None] * outs, axis=0)
+    return o, lse
+
+
+def split_attention_head64(q, k, v, causal, scale, bounds, q_offset=0):
+    """Forward for one head with the keys split at ``bounds`` (0 = b_0 < b_1 < … < b_S = Nk): each chunk
+    [b_s, b_{s+1}) is attended to on its own (plain definition, mask positions shifted by the chunk
+    start), then the chunks are merged with merge_partials64.  Rows with no usable key in a chunk get
+    LSE_s = −inf there.  Returns (o, lse).
+    """
+    q = _as64(q)
+    k = _as64(k)
+    v = _as64(v)
+    parts = []
+    for b0, b1 in zip(bounds[:-1], bounds[1:]):
+        s = scores_head64(q, k[b0:b1], causal, scale, q_offset - b0)
+        m = np.max(s, axis=1)
+        live = np.isfinite(m)
+        e = np.where(live[:, None], np.exp(s - np.where(live, m, 0.0)[:, None]), 0.0)
+        l = np.sum(e, axis=1)
+        o = np.where(live[:, None], (e @ v[b0:b1]) / np.where(live, l, 1.0)[:, None], 0.0)
+        lse = np.where(live, m + np.log(np.where(live, l, 1.0)), -np.inf)
+        parts.append((o, lse))
+    return merge_partials64(parts)

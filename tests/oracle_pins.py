@@ -12,6 +12,12 @@ Sources of the facts:
     tiling keep it exact?";
   * statistics kept for the backward (max and denominator, folded into LSE) — same page, section "How
     does FlashAttention save memory in the backward pass?";
+  * decoding against a key/value cache — glossary entry "flash attention" (paragraph on long-context
+    training and serving) and "FlashAttention: where it matters", section "Where It Matters": the last
+    Nq queries of a sequence against all its keys, checked against the square result's last rows;
+  * merging chunk results — the online-softmax recurrence applied to whole key chunks ("Anatomy ...",
+    section "What is online softmax and how does tiling keep it exact?"), checked in closed form and
+    against attention over all keys;
   * everything else is mathematics: rows of a softmax sum to 1, equal scores give the mean, one key
     gives its value row, shifting all keys by u shifts every score of row i by scale·q_i·u, attention
     is linear in V, a joint key/value permutation is harmless without a mask, and the chain rule,
@@ -258,6 +264,70 @@ def pin_batched_and_rows(orc):
                 assert np.max(np.abs(lrow - lh[rows])) <= 1e-13
 
 
+def pin_decode_rows_of_full(orc):
+    """Decoding the last Nq queries of a sequence against all its keys (query offset Nk − Nq) gives
+    exactly the last Nq rows of the square attention over the whole sequence, causal or not."""
+    for n, n_q, d in ((9, 1, 4), (13, 4, 3), (20, 7, 8), (6, 6, 2)):
+        q, k, v = _qkv(n, d, 40 + n)
+        for causal in (False, True):
+            o, lse = orc.attention_head_fwd64(q, k, v, causal, 0.45)
+            od, ld = orc.attention_head_fwd64(q[n - n_q:], k, v, causal, 0.45, q_offset=n - n_q)
+            assert np.max(np.abs(od - o[n - n_q:])) <= 1e-13
+            assert np.max(np.abs(ld - lse[n - n_q:])) <= 1e-13
+
+
+def pin_decode_single_query(orc):
+    """One query at the end of the sequence sees every key: the causal decode result equals the
+    library softmax over all keys (scipy), and equals the non-causal result."""
+    q, k, v = _qkv(1, 6, 50, n_k=17)
+    s = 0.7 * (k @ q[0])
+    p = scipy.special.softmax(s)
+    o, lse = orc.attention_head_fwd64(q, k, v, True, 0.7, q_offset=16)
+    assert np.max(np.abs(o[0] - p @ v)) <= 1e-13
+    assert abs(lse[0] - scipy.special.logsumexp(s)) <= 1e-13
+    o2, lse2 = orc.attention_head_fwd64(q, k, v, False, 0.7)
+    assert np.max(np.abs(o - o2)) <= 1e-14 and np.max(np.abs(lse - lse2)) <= 1e-14
+
+
+def pin_decode_brute(orc):
+    """With a query offset the numpy forward equals the pure-Python loops (rectangular, causal)."""
+    for n_q, n_k, d in ((1, 5, 2), (3, 7, 3), (4, 4, 2), (2, 9, 4)):
+        r = _rng(60 + n_k)
+        q, k, v = r.standard_normal((n_q, d)), r.standard_normal((n_k, d)), r.standard_normal((n_k, d))
+        for off in sorted({n_k - n_q, 0, 1}):
+            o, lse = orc.attention_head_fwd64(q, k, v, True, 0.8, q_offset=off)
+            ob, lb = orc.brute_attention_head(q.tolist(), k.tolist(), v.tolist(), True, 0.8, off)
+            assert np.max(np.abs(o - np.array(ob))) <= 1e-13
+            assert np.max(np.abs(lse - np.array(lb))) <= 1e-13
+
+
+def pin_merge_closed_form(orc):
+    """Merging chunk results by their softmax mass: chunks with LSE ln 1 and ln 3 and outputs e_0 and
+    e_1 give LSE ln 4 and O = (1/4, 3/4); a chunk with no usable key (LSE −inf) changes nothing."""
+    o, lse = orc.merge_partials64([(np.array([[1.0, 0.0]]), np.array([0.0])),
+                                   (np.array([[0.0, 1.0]]), np.array([math.log(3.0)]))])
+    assert np.max(np.abs(o - np.array([[0.25, 0.75]]))) <= 1e-15
+    assert abs(lse[0] - math.log(4.0)) <= 1e-15
+    o2, lse2 = orc.merge_partials64([(np.array([[0.3, -2.0]]), np.array([1.5])),
+                                     (np.array([[7.0, 7.0]]), np.array([-np.inf]))])
+    assert np.array_equal(o2, np.array([[0.3, -2.0]])) and lse2[0] == 1.5
+
+
+def pin_split_merge(orc):
+    """Attending to key chunks separately and merging the chunk results equals attending to all keys
+    at once, for any chunking, with and without the causal mask and a query offset (chunks that are
+    fully masked for some rows included)."""
+    r = _rng(70)
+    n_q, n_k, d = 5, 23, 4
+    q, k, v = r.standard_normal((n_q, d)), r.standard_normal((n_k, d)), r.standard_normal((n_k, d))
+    for bounds in ([0, 23], [0, 1, 23], [0, 8, 16, 23], [0, 5, 6, 7, 20, 22, 23]):
+        for causal, off in ((False, 0), (True, 18), (True, 3), (True, 0)):
+            o, lse = orc.attention_head_fwd64(q, k, v, causal, 0.55, q_offset=off)
+            os_, ls_ = orc.split_attention_head64(q, k, v, causal, 0.55, bounds, q_offset=off)
+            assert np.max(np.abs(os_ - o)) <= 1e-13, (bounds, causal, off)
+            assert np.max(np.abs(ls_ - lse)) <= 1e-13, (bounds, causal, off)
+
+
 ALL_PINS = [
     pin_softmax_rows,
     pin_library_softmax,
@@ -273,4 +343,9 @@ ALL_PINS = [
     pin_backward_identities,
     pin_brute_force,
     pin_batched_and_rows,
+    pin_decode_rows_of_full,
+    pin_decode_single_query,
+    pin_decode_brute,
+    pin_merge_closed_form,
+    pin_split_merge,
 ]

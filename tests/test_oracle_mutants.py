@@ -19,8 +19,18 @@ SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), 
 # (name, text in the oracle, planted replacement)
 MUTANTS = [
     ("dropped_scale", "s = scale * (q @ k.T)", "s = (q @ k.T)"),
-    ("mask_off_by_one", "s = np.where(j > i, -np.inf, s)", "s = np.where(j >= i, -np.inf, s)"),
-    ("mask_transposed", "s = np.where(j > i, -np.inf, s)", "s = np.where(j < i, -np.inf, s)"),
+    ("mask_off_by_one", "s = np.where(j > q_offset + i, -np.inf, s)",
+     "s = np.where(j >= q_offset + i, -np.inf, s)"),
+    ("mask_transposed", "s = np.where(j > q_offset + i, -np.inf, s)",
+     "s = np.where(j < q_offset + i, -np.inf, s)"),
+    ("decode_offset_ignored", "s = np.where(j > q_offset + i, -np.inf, s)",
+     "s = np.where(j > i, -np.inf, s)"),
+    ("brute_offset_ignored", "if (not causal) or j <= q_offset + i]", "if (not causal) or j <= i]"),
+    ("merge_unweighted", "o = np.sum((w / tot[None, :])[:, :, None] * outs, axis=0)",
+     "o = np.mean(outs, axis=0)"),
+    ("merge_lse_no_max", "lse = mx + np.log(tot)", "lse = np.log(tot)"),
+    ("split_offset_not_shifted", "s = scores_head64(q, k[b0:b1], causal, scale, q_offset - b0)",
+     "s = scores_head64(q, k[b0:b1], causal, scale, q_offset)"),
     ("lse_without_max", "lse = m + np.log(l)", "lse = np.log(l)"),
     ("unnormalised_p", "p = e / l[:, None]", "p = e"),
     ("dv_untransposed", "dv = p.T @ do", "dv = p @ do"),

@@ -26,6 +26,20 @@ def test_inputs_are_deterministic_and_distinct():
     assert not torch.equal(a["v"], a["do"])
 
 
+def test_decode_workloads():
+    w = workloads.DECODE_WORKLOADS
+    assert [x.number for x in w.values()] == [6, 7]
+    assert w["decode_32k"].q_shape() == (4, 32, 1, 128)
+    assert w["specdec_32k"].kv_shape() == (4, 32, 32768, 128)
+    assert w["decode_32k"].kv_bytes() == 2 * 4 * 32 * 32768 * 128 * 2
+    a = workloads.make_decode_inputs("specdec_32k", B=1, H=2, Nk=70)
+    b = workloads.make_decode_inputs("specdec_32k", B=1, H=2, Nk=70)
+    assert a["q"].shape == (1, 2, 8, 128) and a["k"].shape == (1, 2, 70, 128)
+    for key in ("q", "k", "v"):
+        assert a[key].dtype == torch.bfloat16 and torch.equal(a[key], b[key])
+    assert not torch.equal(a["k"], a["v"])
+
+
 def _bf16_rne_bits(x):
     """Independent float32 → bfloat16 round-to-nearest-even on the bit pattern (finite inputs)."""
     u = x.astype(np.float32).view(np.uint32).astype(np.uint64)

@@ -17,8 +17,18 @@ long_16k  1, 32, 16384, 128      yes     forward + backward, bf16, one ×8 key p
 fp8_8k    4, 32, 8192, 128       yes     forward only, e4m3 Q/K/V with per-tensor scales, O bf16
 ========  =====================  ======  ========================================================
 
+Decoding workloads (queries [B, H, Nq, d] against a key/value cache [B, H, Nk, d]; the queries are the
+last Nq positions of the sequence, so with the causal mask query i may use keys j ≤ Nk − Nq + i):
+
+===========  ==========================  ======  ===================================================
+name         B, H, Nq, Nk, d             causal  what runs
+===========  ==========================  ======  ===================================================
+decode_32k   4, 32, 1, 32768, 128        yes     one new token per sequence, bf16
+specdec_32k  4, 32, 8, 32768, 128        yes     8 draft tokens verified at once (speculative), bf16
+===========  ==========================  ======  ===================================================
+
 Seeds: tensor t of workload c uses ``torch.Generator().manual_seed(1000*c + t)`` with c the workload
-number 1..5 and t = 0 (Q), 1 (K), 2 (V), 3 (dO), 4 (positions of the enlarged keys).  Values are drawn
+number 1..7 and t = 0 (Q), 1 (K), 2 (V), 3 (dO), 4 (positions of the enlarged keys).  Values are drawn
 as float32 N(0, 1) on the CPU and rounded to the storage type, so every consumer sees identical inputs.
 """
 
@@ -72,6 +82,55 @@ WORKLOADS = {
         Workload(5, "fp8_8k", 4, 32, 8192, 128, causal=True, backward=False, fp8=True),
     ]
 }
+
+
+@dataclass(frozen=True)
+class DecodeWorkload:
+    number: int
+    name: str
+    B: int
+    H: int
+    Nq: int
+    Nk: int
+    d: int
+    causal: bool
+
+    @property
+    def scale(self):
+        return 1.0 / math.sqrt(self.d)
+
+    def q_shape(self, B=None, H=None):
+        return (self.B if B is None else B, self.H if H is None else H, self.Nq, self.d)
+
+    def kv_shape(self, B=None, H=None, Nk=None):
+        return (self.B if B is None else B, self.H if H is None else H,
+                self.Nk if Nk is None else Nk, self.d)
+
+    def kv_bytes(self, B=None, H=None, Nk=None):
+        """Bytes of the bf16 key and value cache: what one decode step must read at least once."""
+        b, h, n, d = self.kv_shape(B, H, Nk)
+        return 2 * b * h * n * d * 2
+
+
+DECODE_WORKLOADS = {
+    w.name: w
+    for w in [
+        DecodeWorkload(6, "decode_32k", 4, 32, 1, 32768, 128, causal=True),
+        DecodeWorkload(7, "specdec_32k", 4, 32, 8, 32768, 128, causal=True),
+    ]
+}
+
+
+def make_decode_inputs(name, B=None, H=None, Nk=None):
+    """Inputs of a decoding workload as CPU bf16 tensors {"q", "k", "v"}, optionally at a reduced B,
+    H or cache length Nk (same seeds)."""
+    w = DECODE_WORKLOADS[name]
+    c = w.number
+    return {
+        "q": to_bf16(randn_f32(w.q_shape(B, H), 1000 * c + 0)),
+        "k": to_bf16(randn_f32(w.kv_shape(B, H, Nk), 1000 * c + 1)),
+        "v": to_bf16(randn_f32(w.kv_shape(B, H, Nk), 1000 * c + 2)),
+    }
 
 
 def _gen(seed):
