@@ -198,6 +198,56 @@ def traffic_sweep(fa, torch, steps):
         del q, k, v, o, lse
 
 
+def decode_measure(fa, workloads, lib, steps, warmup):
+    """Secondary measurement: decoding against a key/value cache (both decoding workloads), timed
+    with events around fa_decode (split and merge kernels).  HBM-bound: priced against 8 TB/s with
+    the algorithmic bytes (cache read once, Q read, O and LSE written).  The inputs are N(0,1) bf16
+    drawn on the device from a seeded generator (timing does not depend on the values; the parity
+    tests use the CPU-drawn workload inputs)."""
+    import torch
+    out = {}
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    for name in ("decode_32k", "specdec_32k"):
+        w = workloads.DECODE_WORKLOADS[name]
+        log(f"[bench] secondary: {name} decode B={w.B} H={w.H} Nq={w.Nq} Nk={w.Nk} d={w.d}")
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(1000 * w.number)
+        q = torch.randn(w.q_shape(), generator=gen, device=dev).to(torch.bfloat16)
+        k = torch.randn(w.kv_shape(), generator=gen, device=dev).to(torch.bfloat16)
+        v = torch.randn(w.kv_shape(), generator=gen, device=dev).to(torch.bfloat16)
+        o = torch.empty_like(q)
+        lse = torch.empty(w.q_shape()[:3], dtype=torch.float32, device=dev)
+        ws_bytes = fa.decode_workspace_bytes(w.B, w.H, w.Nq, w.Nk, w.d)
+        ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+
+        def run():
+            code = lib.fa_decode(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                 lse.data_ptr(), ws.data_ptr(), ws_bytes, w.B, w.H, w.Nq, w.Nk, w.d,
+                                 int(w.causal), w.scale, stream.cuda_stream)
+            if code != 0:
+                raise fa.FaError("fa_decode", code, fa.status_str(code))
+
+        for _ in range(warmup):
+            run()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record(stream)
+        for _ in range(steps):
+            run()
+        ev[1].record(stream)
+        torch.cuda.synchronize(dev)
+        ms = ev[0].elapsed_time(ev[1]) / steps
+        algo = w.kv_bytes() + 2 * q.numel() * 2 + lse.numel() * 4
+        gbs = algo / (ms * 1e-3) / 1e9
+        out[name + "_decode"] = {"workload": name, "kernels": ["decode_split_kernel", "decode_merge_kernel"],
+                                 "ms": ms, "achieved_gbs": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                 "frac": gbs / HBM_PEAK_GBS, "bound": "hbm",
+                                 "algorithmic_bytes": algo, "workspace_bytes": ws_bytes}
+        del q, k, v, o, lse, ws
+        torch.cuda.empty_cache()
+    return out
+
+
 def fp8_forward(fa, workloads, lib, steps, warmup):
     """Secondary measurement: the FP8 forward on its workload (fp8_8k), timed with events."""
     import torch
@@ -244,6 +294,8 @@ def main():
                     help="seconds of oracle work for the cpu_baseline leg (0 skips it)")
     ap.add_argument("--no-fp8", action="store_true",
                     help="skip the secondary FP8 forward measurement (fp8_8k workload)")
+    ap.add_argument("--no-decode", action="store_true",
+                    help="skip the secondary decoding measurements (decode_32k, specdec_32k)")
     ap.add_argument("--traffic-sweep", action="store_true",
                     help="instead of the bench, run the forward at N = 1k..16k (B=1, H=32, d=128, "
                          "causal) `--steps` times each, for HBM byte counters")
@@ -388,6 +440,8 @@ def main():
     secondary = {}
     if not args.no_fp8:
         secondary["fp8_8k_fwd"] = fp8_forward(fa, workloads, lib, args.steps, args.warmup)
+    if not args.no_decode:
+        secondary.update(decode_measure(fa, workloads, lib, args.steps, args.warmup))
 
     cpu = None
     if args.cpu_budget > 0:

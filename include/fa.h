@@ -114,6 +114,33 @@ fa_status fa_bwd_dq(const void* q, const void* k, const void* v, const float* ls
                     int B, int H, int N, int d, int causal, float softmax_scale,
                     hipStream_t stream);
 
+/* ---------------------------------------------------------------------------------------------------
+ * Decoding against a key/value cache: a few new queries per (batch, head) attend over Nk cached keys,
+ * the inference use the pages pair FlashAttention with ("flash attention" glossary entry, paragraph on
+ * long-context training and serving; "FlashAttention: where it matters", section "Where It Matters":
+ * long-context inference and speculative decoding).
+ *
+ *   q, o     [B, H, Nq, d] bf16, 1 ≤ Nq ≤ 32 (one new token, or a few draft tokens verified at once)
+ *   k, v     [B, H, Nk, d] bf16, the cache, Nk ≥ Nq
+ *   lse      [B, H, Nq] fp32, natural-log logsumexp of the scaled scores over the keys each query uses
+ *   causal   the queries are the last Nq positions of the sequence: causal != 0 lets query i use key j
+ *            only when j ≤ Nk − Nq + i; causal == 0 lets every query use all Nk keys
+ *   workspace  device buffer of at least fa_decode_workspace_bytes(B, H, Nq, Nk, d) bytes, 256-byte
+ *            aligned, owned by the caller; it receives per-chunk partial results (the keys are split
+ *            into chunks attended to in parallel and merged by their softmax mass, the online-softmax
+ *            recurrence of "Anatomy of a FlashAttention Kernel" applied to whole chunks) and needs no
+ *            initialisation; its contents after the call are unspecified.
+ *   d ∈ {64, 128}; other conventions as above.  Results are deterministic.
+ *
+ * Errors: FA_ERR_NULL (a tensor pointer is NULL), FA_ERR_SHAPE (B or H < 1, Nq outside [1, 32], Nk < Nq,
+ * or the cache too large for 32-bit per-head offsets), FA_ERR_UNSUPPORTED (d, or a scale that is not
+ * finite and positive), FA_ERR_WORKSPACE (workspace NULL or too small), FA_ERR_ALIGN, FA_ERR_LAUNCH.
+ * fa_decode_workspace_bytes returns 0 for shapes fa_decode rejects. */
+size_t fa_decode_workspace_bytes(int B, int H, int Nq, int Nk, int d);
+fa_status fa_decode(const void* q, const void* k, const void* v, void* o, float* lse,
+                    void* workspace, size_t workspace_bytes, int B, int H, int Nq, int Nk, int d,
+                    int causal, float softmax_scale, hipStream_t stream);
+
 /* A static, human-readable name for a status code (never NULL). */
 const char* fa_status_str(fa_status status);
 

@@ -12,6 +12,8 @@ Entry points (same names as the C ABI, without the ``fa_`` prefix):
   bwd_workspace_bytes(B, H, N, d) -> int
   bwd_preprocess / bwd_dkdv / bwd_dq — the three phases fa_bwd runs, for timing them apart
   status_str(code) -> str
+  decode(q, k, v, causal, scale=None, workspace=None) -> (o, lse)   (q: [B,H,Nq,d], k/v: [B,H,Nk,d])
+  decode_workspace_bytes(B, H, Nq, Nk, d) -> int
   device_info(device=0) -> (compute units, peak clock kHz), for pricing measurements
 """
 
@@ -22,7 +24,8 @@ import os
 import torch
 
 __all__ = ["fwd", "fwd_fp8", "bwd", "bwd_workspace_bytes", "bwd_preprocess", "bwd_dkdv",
-           "bwd_dq", "status_str", "device_info", "FaError", "library", "LIB_PATH"]
+           "bwd_dq", "decode", "decode_workspace_bytes", "status_str", "device_info", "FaError",
+           "library", "LIB_PATH"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
 
@@ -68,6 +71,10 @@ def library():
         lib.fa_status_str.restype = ctypes.c_char_p
         lib.fa_device_info.argtypes = [i, vp, vp]
         lib.fa_device_info.restype = i
+        lib.fa_decode_workspace_bytes.argtypes = [i, i, i, i, i]
+        lib.fa_decode_workspace_bytes.restype = sz
+        lib.fa_decode.argtypes = [vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, i, f, vp]
+        lib.fa_decode.restype = i
         _lib = lib
     return _lib
 
@@ -124,6 +131,36 @@ def fwd(q, k, v, causal, scale=None):
                                 lse.data_ptr(), B, H, N, d, int(bool(causal)), _scale(scale, d),
                                 _stream(q.device))
     _check("fa_fwd", code)
+    return o, lse
+
+
+def decode_workspace_bytes(B, H, Nq, Nk, d):
+    """Bytes of workspace fa_decode needs (0 for a shape it rejects)."""
+    return int(library().fa_decode_workspace_bytes(B, H, Nq, Nk, d))
+
+
+def decode(q, k, v, causal, scale=None, workspace=None):
+    """Decoding against a key/value cache: q [B,H,Nq,d] (1 ≤ Nq ≤ 32, the last Nq positions of the
+    sequence), k and v [B,H,Nk,d] bf16.  Returns (o bf16 [B,H,Nq,d], lse fp32 [B,H,Nq])."""
+    _require(q, "q", torch.bfloat16)
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, Nq, d]")
+    B, H, Nq, d = q.shape
+    _require(k, "k", torch.bfloat16)
+    if k.dim() != 4 or k.shape[0] != B or k.shape[1] != H or k.shape[3] != d:
+        raise ValueError(f"k has shape {tuple(k.shape)}, expected [{B}, {H}, Nk, {d}]")
+    Nk = k.shape[2]
+    _require(v, "v", torch.bfloat16, k.shape)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    ws_bytes = decode_workspace_bytes(B, H, Nq, Nk, d)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=q.device)
+    with torch.cuda.device(q.device):
+        code = library().fa_decode(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                   lse.data_ptr(), workspace.data_ptr(), workspace.numel(), B, H,
+                                   Nq, Nk, d, int(bool(causal)), _scale(scale, d), _stream(q.device))
+    _check("fa_decode", code)
     return o, lse
 
 

@@ -45,10 +45,10 @@ const char* fa_status_str(fa_status status) {
   switch (status) {
     case FA_OK: return "FA_OK";
     case FA_ERR_NULL: return "FA_ERR_NULL: a required pointer is NULL";
-    case FA_ERR_SHAPE: return "FA_ERR_SHAPE: B, H or N out of range";
+    case FA_ERR_SHAPE: return "FA_ERR_SHAPE: B, H, N (or Nq, Nk) out of range";
     case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: head dimension, scale or descale not supported";
     case FA_ERR_ALIGN: return "FA_ERR_ALIGN: a pointer is not suitably aligned";
-    case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE: backward workspace missing or too small";
+    case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE: workspace missing or too small";
     case FA_ERR_LAUNCH: return "FA_ERR_LAUNCH: the HIP runtime rejected a kernel launch";
   }
   return "unknown fa_status";
@@ -169,6 +169,31 @@ fa_status fa_bwd_dq(const void* q, const void* k, const void* v, const float* ls
   a.causal = causal ? 1 : 0;
   a.scale = softmax_scale;
   return fa::launch_bwd_dq(a, stream) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+size_t fa_decode_workspace_bytes(int B, int H, int Nq, int Nk, int d) {
+  if (B < 1 || H < 1 || Nq < 1 || Nq > 32 || Nk < Nq) return 0;
+  if (d != 64 && d != 128) return 0;
+  return fa::decode_workspace_bytes(B, H, Nq, Nk, d);
+}
+
+fa_status fa_decode(const void* q, const void* k, const void* v, void* o, float* lse,
+                    void* workspace, size_t workspace_bytes, int B, int H, int Nq, int Nk, int d,
+                    int causal, float softmax_scale, hipStream_t stream) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+  if (B < 1 || H < 1 || Nq < 1 || Nq > 32 || Nk < Nq) return FA_ERR_SHAPE;
+  fa_status st = check_shape(B, H, Nk, d, 2);  // the cache: per-head offsets, totals, grid
+  if (st != FA_OK) return st;
+  const fa::DecodeSplit sp = fa::decode_split(B, H, Nq, Nk);
+  if ((uint64_t)B * (uint64_t)H * (uint64_t)sp.S >= (1ull << 31)) return FA_ERR_SHAPE;
+  if (!good_scale(softmax_scale)) return FA_ERR_UNSUPPORTED;
+  if (!workspace || workspace_bytes < fa::decode_workspace_bytes(B, H, Nq, Nk, d))
+    return FA_ERR_WORKSPACE;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+      !aligned(lse, 16) || !aligned(workspace, 256))
+    return FA_ERR_ALIGN;
+  fa::DecodeArgs a{q, k, v, o, lse, workspace, B, H, Nq, Nk, d, causal ? 1 : 0, softmax_scale};
+  return fa::launch_decode(a, stream) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
 fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,

@@ -164,35 +164,41 @@ __device__ inline bf16x8 tr_frag(const char* lds, const FragOffsets<D>& fo, int 
 // the buffer resource `r`) into LDS by NT threads, without passing through registers
 // (buffer_load_dwordx4 ... lds: lane i of a wave writes LDS bytes [16 i, 16 i + 16) after the
 // wave-uniform base).  Rows past the buffer's end read as zeros.  The 16-byte chunk c of row r is
-// stored at physical chunk c ^ swz(r), where swz depends only on r mod 16.  Each issue round covers
-// NT / (ROW_BYTES / 16) rows, a multiple of 16, so a lane's offset within a round is the same in every
-// round and every tile: it is computed once, here, and each load of a copy adds a scalar row offset
-// to it (one vector add; the row offset stays in the range-checked vector offset so the zero fill
-// of ragged tails still applies).  Completion: wait_vmem_all().
+// stored at physical chunk c ^ swz(r), where swz depends only on r mod 16.  An issue round covers
+// NT / (ROW_BYTES / 16) rows; the swizzle repeats every 16 rows, so a lane's offset within a round
+// takes PAT = max(1, 16 / rows-per-round) values, computed once, here, and each load of a copy adds
+// a scalar row offset to one of them (one vector add; the row offset stays in the range-checked
+// vector offset so the zero fill of ragged tails still applies).  Completion: wait_vmem_all().
 template <int ROW_BYTES, int ROWS, int NT>
 struct TileCopy {
   static constexpr int CPR = ROW_BYTES / 16;        // 16-byte chunks per row
   static constexpr int ROUNDS = ROWS * CPR / NT;    // loads per thread
   static constexpr int ROUND_ROWS = NT / CPR;       // rows per round
+  static constexpr int PAT = ROUND_ROWS >= 16 ? 1 : 16 / ROUND_ROWS;  // distinct lane offsets
   static_assert(ROWS * CPR % NT == 0, "tile must split evenly over the threads");
-  static_assert(ROUND_ROWS % 16 == 0, "the swizzle must repeat across rounds");
-  uint32_t voff;  // this lane's byte offset inside a round
+  static_assert(ROUND_ROWS % 16 == 0 || 16 % ROUND_ROWS == 0, "the swizzle must repeat across rounds");
+  static_assert(ROUNDS % PAT == 0, "whole swizzle periods per copy");
+  uint32_t voff[PAT];  // this lane's byte offset inside round p of each swizzle period
   int wave;
   template <class Swz>
   __device__ TileCopy(int tid, Swz swz) {
     wave = wave_index(tid);
-    const int slot = wave * 64 + (tid & 63);  // physical 16-byte slot within round 0
-    const int row = slot / CPR, pc = slot % CPR;
-    voff = (uint32_t)(row * ROW_BYTES + 16 * (pc ^ swz(row)));  // logical chunk held by slot pc
+    const int slot = wave * 64 + (tid & 63);  // physical 16-byte slot within a round
+    const int pc = slot % CPR;
+#pragma unroll
+    for (int p = 0; p < PAT; ++p) {
+      const int row = p * ROUND_ROWS + slot / CPR;
+      voff[p] = (uint32_t)(row * ROW_BYTES + 16 * (pc ^ swz(row)));  // logical chunk held by slot pc
+    }
   }
   template <class T>
   __device__ void operator()(__amdgpu_buffer_rsrc_t r, int row0, T* lds) const {
 #pragma unroll
     for (int i = 0; i < ROUNDS; ++i) {
-      const uint32_t base = (uint32_t)(row0 + i * ROUND_ROWS) * (uint32_t)ROW_BYTES;
+      const uint32_t base = (uint32_t)(row0 + (i / PAT) * PAT * ROUND_ROWS) * (uint32_t)ROW_BYTES;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           r, (__attribute__((address_space(3))) void*)((char*)lds + (i * (NT / 64) + wave) * 1024),
-          16, voff + base, 0, 0, 0);
+          16, (uint32_t)(voff[i % PAT] + base), 0, 0, 0);
     }
   }
 };

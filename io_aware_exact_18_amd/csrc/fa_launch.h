@@ -42,11 +42,51 @@ struct BwdArgs {
   float scale;
 };
 
+struct DecodeArgs {
+  const void* q;  // [B,H,Nq,d] bf16
+  const void* k;  // [B,H,Nk,d] bf16
+  const void* v;  // [B,H,Nk,d] bf16
+  void* o;        // [B,H,Nq,d] bf16
+  float* lse;     // [B,H,Nq] fp32
+  void* workspace;
+  int B, H, Nq, Nk, d, causal;
+  float scale;
+};
+
+// Split-KV decomposition of a decode call: S chunks of split_len keys (a multiple of 32; the last
+// chunk may be shorter).  Enough chunks for about 2048 workgroups over the device, each chunk at least
+// 256 keys long.
+struct DecodeSplit {
+  int S;
+  int split_len;
+};
+inline DecodeSplit decode_split(int B, int H, int Nq, int Nk) {
+  (void)Nq;
+  const long bh = (long)B * H;
+  long s = (2048 + bh - 1) / bh;
+  const long by_len = ((long)Nk + 255) / 256;
+  if (s > by_len) s = by_len;
+  if (s < 1) s = 1;
+  long len = ((long)Nk + s - 1) / s;
+  len = (len + 31) / 32 * 32;
+  DecodeSplit r;
+  r.split_len = (int)len;
+  r.S = (int)(((long)Nk + len - 1) / len);
+  return r;
+}
+// Workspace of a decode call: per (batch·head, chunk, query) the unnormalised output (d fp32) and the
+// chunk's row maximum and row sum (2 fp32), rounded up to 256 bytes.
+inline size_t decode_workspace_bytes(int B, int H, int Nq, int Nk, int d) {
+  const DecodeSplit sp = decode_split(B, H, Nq, Nk);
+  return (((size_t)B * H * sp.S * Nq * ((size_t)d + 2) * sizeof(float)) + 255u) & ~(size_t)255u;
+}
+
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_fwd_fp8(const Fp8FwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd_pre(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t stream);
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 
 // Backward workspace: the fp32 [B,H,N] array D, rounded up to 256 bytes.
 inline size_t round_up_256(size_t x) { return (x + 255u) & ~(size_t)255u; }

@@ -33,6 +33,9 @@ def lib():
     lib.fa_status_str.argtypes = [i]
     lib.fa_status_str.restype = ctypes.c_char_p
     lib.fa_device_info.argtypes = [i, vp, vp]
+    lib.fa_decode_workspace_bytes.argtypes = [i, i, i, i, i]
+    lib.fa_decode_workspace_bytes.restype = sz
+    lib.fa_decode.argtypes = [vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, i, f, vp]
     return lib
 
 
@@ -40,7 +43,8 @@ def test_exports_match_header(lib):
     text = open(HEADER).read()
     declared = set(re.findall(r"^\s*(?:fa_status|size_t|const char\*)\s+(fa_\w+)\s*\(", text, re.M))
     assert declared == {"fa_fwd", "fa_fwd_fp8", "fa_bwd_workspace_bytes", "fa_bwd", "fa_status_str",
-                        "fa_bwd_preprocess", "fa_bwd_dkdv", "fa_bwd_dq", "fa_device_info"}
+                        "fa_bwd_preprocess", "fa_bwd_dkdv", "fa_bwd_dq", "fa_device_info",
+                        "fa_decode", "fa_decode_workspace_bytes"}
     for name in declared:
         assert hasattr(lib, name), name
 
@@ -141,3 +145,51 @@ def test_binding_fails_loudly_without_tensors_on_gpu():
     q = torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16)  # a CPU tensor: rejected, no fallback
     with pytest.raises(ValueError):
         fa.fwd(q, q, q, causal=False)
+
+
+# ------------------------------------------------------------------------------------------------
+# Decoding entry points.
+
+def _decode_split(B, H, Nk):
+    """The chunking fa.h documents for fa_decode: about 2048 workgroups, chunks of ≥ 256 keys,
+    chunk length a multiple of 32."""
+    bh = B * H
+    s = max(1, min(-(-2048 // bh), -(-Nk // 256)))
+    length = -(-Nk // s)
+    length = -(-length // 32) * 32
+    return -(-Nk // length), length
+
+
+def test_decode_workspace_formula(lib):
+    for B, H, Nq, Nk, d in ((1, 1, 1, 1, 64), (4, 32, 1, 32768, 128), (4, 32, 8, 32768, 128),
+                            (1, 2, 3, 3000, 64), (2, 3, 32, 257, 128), (64, 64, 4, 100, 128)):
+        S, length = _decode_split(B, H, Nk)
+        assert (S - 1) * length < Nk <= S * length
+        want = -(-(B * H * S * Nq * (d + 2) * 4) // 256) * 256
+        assert lib.fa_decode_workspace_bytes(B, H, Nq, Nk, d) == want, (B, H, Nq, Nk, d)
+    for bad in ((0, 1, 1, 8, 64), (1, 1, 0, 8, 64), (1, 1, 33, 64, 64), (1, 1, 9, 8, 64),
+                (1, 1, 1, 8, 96)):
+        assert lib.fa_decode_workspace_bytes(*bad) == 0, bad
+
+
+def decode(lib, q=P, k=P, v=P, o=P, lse=P, ws=P, ws_bytes=1 << 30, B=1, H=1, Nq=1, Nk=64, d=64,
+           causal=1, scale=0.125):
+    return lib.fa_decode(q, k, v, o, lse, ws, ws_bytes, B, H, Nq, Nk, d, causal, scale, None)
+
+
+def test_decode_rejections(lib):
+    assert decode(lib, q=None) == NULL
+    assert decode(lib, lse=None) == NULL
+    assert decode(lib, Nq=0) == SHAPE
+    assert decode(lib, Nq=33, Nk=64) == SHAPE
+    assert decode(lib, Nq=9, Nk=8) == SHAPE
+    assert decode(lib, B=0) == SHAPE
+    assert decode(lib, Nk=1 << 23, d=128) == SHAPE  # per-head cache past 32-bit offsets
+    assert decode(lib, d=96) == UNSUP
+    assert decode(lib, scale=0.0) == UNSUP
+    assert decode(lib, scale=math.inf) == UNSUP
+    assert decode(lib, ws=None) == WORKSPACE
+    need = lib.fa_decode_workspace_bytes(1, 1, 1, 64, 64)
+    assert decode(lib, ws_bytes=need - 1) == WORKSPACE
+    assert decode(lib, k=MIS) == ALIGN
+    assert decode(lib, ws=P + 16) == ALIGN
