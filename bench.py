@@ -283,6 +283,68 @@ def fp8_forward(fa, workloads, lib, steps, warmup):
             "flops": w.fwd_flops()}
 
 
+def fwd_bwd_secondary(fa, workloads, lib, name, steps, warmup):
+    """Secondary measurement: forward + backward of another bf16 workload (d256_4k: head dimension
+    256), each phase bracketed by events; TFLOP/s by the same FLOP convention as the headline."""
+    import torch
+    w = workloads.WORKLOADS[name]
+    B, H, N, d = w.shape()
+    log(f"[bench] secondary: {name} forward+backward B={B} H={H} N={N} d={d} causal={w.causal}")
+    inp = workloads.make_inputs(name)
+    dev = torch.device("cuda:0")
+    q, k, v, do = (inp[x].to(dev) for x in ("q", "k", "v", "do"))
+    del inp
+    o, dq, dk, dv = (torch.empty_like(q) for _ in range(4))
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    ws_bytes = fa.bwd_workspace_bytes(B, H, N, d)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    sp = stream.cuda_stream
+    c = int(w.causal)
+
+    def check(fn, code):
+        if code != 0:
+            raise fa.FaError(fn, code, fa.status_str(code))
+
+    def step(ev):
+        ev[0].record(stream)
+        check("fa_fwd", lib.fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                   lse.data_ptr(), B, H, N, d, c, w.scale, sp))
+        ev[1].record(stream)
+        check("fa_bwd_preprocess", lib.fa_bwd_preprocess(o.data_ptr(), do.data_ptr(), ws.data_ptr(),
+                                                         ws_bytes, B, H, N, d, sp))
+        ev[2].record(stream)
+        check("fa_bwd_dkdv", lib.fa_bwd_dkdv(q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                             lse.data_ptr(), do.data_ptr(), dk.data_ptr(),
+                                             dv.data_ptr(), ws.data_ptr(), ws_bytes, B, H, N, d, c,
+                                             w.scale, sp))
+        ev[3].record(stream)
+        check("fa_bwd_dq", lib.fa_bwd_dq(q.data_ptr(), k.data_ptr(), v.data_ptr(), lse.data_ptr(),
+                                         do.data_ptr(), dq.data_ptr(), ws.data_ptr(), ws_bytes, B,
+                                         H, N, d, c, w.scale, sp))
+        ev[4].record(stream)
+
+    spare = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+    for _ in range(warmup):
+        step(spare)
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
+    for i in range(steps):
+        step(events[i])
+    torch.cuda.synchronize(dev)
+    ph = [sum(e[i].elapsed_time(e[i + 1]) for e in events) / steps for i in range(4)]
+    step_ms = sum(e[0].elapsed_time(e[4]) for e in events) / steps
+    fwd_f, bwd_f = w.fwd_flops(), w.bwd_flops()
+    out = {"workload": name, "ms": step_ms, "tflops": (fwd_f + bwd_f) / (step_ms * 1e-3) / 1e12,
+           "peak": BF16_PEAK_TFLOPS, "bound": "mfma", "flops": fwd_f + bwd_f,
+           "phases_ms": {"fwd": ph[0], "bwd_preprocess": ph[1], "bwd_dkdv": ph[2], "bwd_dq": ph[3]},
+           "fwd_tflops": fwd_f / (ph[0] * 1e-3) / 1e12,
+           "bwd_tflops": bwd_f / ((ph[1] + ph[2] + ph[3]) * 1e-3) / 1e12}
+    out["frac"] = out["tflops"] / BF16_PEAK_TFLOPS
+    del q, k, v, do, o, dq, dk, dv, lse, ws
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -294,6 +356,8 @@ def main():
                     help="seconds of oracle work for the cpu_baseline leg (0 skips it)")
     ap.add_argument("--no-fp8", action="store_true",
                     help="skip the secondary FP8 forward measurement (fp8_8k workload)")
+    ap.add_argument("--no-d256", action="store_true",
+                    help="skip the secondary head-dimension-256 measurement (d256_4k workload)")
     ap.add_argument("--no-decode", action="store_true",
                     help="skip the secondary decoding measurements (decode_32k, specdec_32k)")
     ap.add_argument("--traffic-sweep", action="store_true",
@@ -440,6 +504,9 @@ def main():
     secondary = {}
     if not args.no_fp8:
         secondary["fp8_8k_fwd"] = fp8_forward(fa, workloads, lib, args.steps, args.warmup)
+    if not args.no_d256:
+        secondary["d256_4k_fwd_bwd"] = fwd_bwd_secondary(fa, workloads, lib, "d256_4k", args.steps,
+                                                         args.warmup)
     if not args.no_decode:
         secondary.update(decode_measure(fa, workloads, lib, args.steps, args.warmup))
 

@@ -62,15 +62,20 @@ __global__ __launch_bounds__(kThreads) void bwd_pre_kernel(const bf16* __restric
 }
 
 // ---------------------------------------------------------------------------------------------------
-// 2. dK, dV.
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(
+// 2. dK, dV.  OUT selects the outputs: 1 = dV, 2 = dK, 3 = both.  Head dimension 256 runs two passes
+// (dV, then dK): with both, the dKᵀ and dVᵀ accumulators alone would take all of a wave's 512
+// registers' worth of room it needs for the K fragments and the step's tiles; the dV pass needs
+// neither V nor dP, and the extra cost is one more S product per step.
+template <int D, bool CAUSAL, int OUT>
+__global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void bwd_dkdv_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     const float* __restrict__ LSE, const bf16* __restrict__ dO, const float* __restrict__ Delta,
     bf16* __restrict__ dK, bf16* __restrict__ dV, int N, int nkt, float scale, float scale_log2,
     int remap) {
   constexpr int KSTEPS = D / 16;
   constexpr int DB = D / 32;
+  constexpr bool WANT_DV = (OUT & 1) != 0;
+  constexpr bool WANT_DK = (OUT & 2) != 0;
   // Q and dO tiles (tile_off<D> layout) and the tile's base-2 LSE and D values (first 32 of 64 used),
   // double-buffered; separate LDS objects so reads of one buffer never wait for the LDS-DMA copy
   // filling the other.
@@ -82,7 +87,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(
   __shared__ __attribute__((aligned(256))) float l1s[64];
   __shared__ __attribute__((aligned(256))) float d0s[64];
   __shared__ __attribute__((aligned(256))) float d1s[64];
-  __shared__ __attribute__((aligned(1024))) bf16 vts[kBKV * D];  // the workgroup's V rows
+  __shared__ __attribute__((aligned(1024))) bf16 vts[WANT_DK ? kBKV * D : 8];  // the workgroup's V rows
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -113,7 +118,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(
 #pragma unroll
   for (int s = 0; s < KSTEPS; ++s)
     kf[s] = __builtin_bit_cast(bf16x8, buf_load16(rk, (uint32_t)(kj * D + 16 * s + 8 * g) * 2u));
-  {
+  if constexpr (WANT_DK) {
     const BfTileCopy<D, kBKV, kThreads> copy_v(tid);
     copy_v(make_rsrc(V + head, head_bytes), k0, vts);
   }
@@ -170,8 +175,9 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(
 #pragma unroll
       for (int s = 0; s < KSTEPS; ++s) {
         sacc = mfma_32x32x16(row_frag<D>(qs, fo, 0, s), kf[s], sacc);
-        pacc = mfma_32x32x16(row_frag<D>(dos, fo, 0, s), row_frag<D>((const char*)vts, fo, wave, s),
-                             pacc);
+        if constexpr (WANT_DK)
+          pacc = mfma_32x32x16(row_frag<D>(dos, fo, 0, s), row_frag<D>((const char*)vts, fo, wave, s),
+                               pacc);
       }
       // Element r: query qb + 8(r/4) + 4g + (r%4), key kj.  Masked scores become -inf (P = 0) in a
       // wave-uniform branch taken only by diagonal and ragged tiles.
@@ -191,7 +197,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(
           const int r = 4 * r4 + t;
           const float p = exp2_fast(fmaf(sacc[r], scale_log2, -l4[t]));  // staged LSE is base 2
           sacc[r] = p;
-          pacc[r] = p * (pacc[r] - d4[t]);  // dS without the scale
+          if constexpr (WANT_DK) pacc[r] = p * (pacc[r] - d4[t]);  // dS without the scale
         }
       }
       bf16x8 pb[2], dsb[2];  // k-step ks covers queries 16ks + 8(e/4) + 4g + (e%4)
@@ -207,8 +213,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(
       for (int b = 0; b < DB; ++b) {
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-          dva[b] = mfma_32x32x16(tr_frag<D>(dos, fo, ks, b), pb[ks], dva[b]);
-          dka[b] = mfma_32x32x16(tr_frag<D>(qs, fo, ks, b), dsb[ks], dka[b]);
+          if constexpr (WANT_DV) dva[b] = mfma_32x32x16(tr_frag<D>(dos, fo, ks, b), pb[ks], dva[b]);
+          if constexpr (WANT_DK) dka[b] = mfma_32x32x16(tr_frag<D>(qs, fo, ks, b), dsb[ks], dka[b]);
         }
       }
     }
@@ -230,13 +236,18 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(
     for (int b = 0; b < DB; ++b)
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
-        u32x2 wk, wv;
-        wk[0] = pack_bf16x2(dka[b][4 * r4 + 0] * scale, dka[b][4 * r4 + 1] * scale);
-        wk[1] = pack_bf16x2(dka[b][4 * r4 + 2] * scale, dka[b][4 * r4 + 3] * scale);
-        wv[0] = pack_bf16x2(dva[b][4 * r4 + 0], dva[b][4 * r4 + 1]);
-        wv[1] = pack_bf16x2(dva[b][4 * r4 + 2], dva[b][4 * r4 + 3]);
-        *(u32x2*)&dkr[32 * b + 8 * r4 + 4 * g] = wk;
-        *(u32x2*)&dvr[32 * b + 8 * r4 + 4 * g] = wv;
+        if constexpr (WANT_DK) {
+          u32x2 wk;
+          wk[0] = pack_bf16x2(dka[b][4 * r4 + 0] * scale, dka[b][4 * r4 + 1] * scale);
+          wk[1] = pack_bf16x2(dka[b][4 * r4 + 2] * scale, dka[b][4 * r4 + 3] * scale);
+          *(u32x2*)&dkr[32 * b + 8 * r4 + 4 * g] = wk;
+        }
+        if constexpr (WANT_DV) {
+          u32x2 wv;
+          wv[0] = pack_bf16x2(dva[b][4 * r4 + 0], dva[b][4 * r4 + 1]);
+          wv[1] = pack_bf16x2(dva[b][4 * r4 + 2], dva[b][4 * r4 + 3]);
+          *(u32x2*)&dvr[32 * b + 8 * r4 + 4 * g] = wv;
+        }
       }
   }
 }
@@ -244,7 +255,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(
 // ---------------------------------------------------------------------------------------------------
 // 3. dQ.
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
+__global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void bwd_dq_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     const float* __restrict__ LSE, const bf16* __restrict__ dO, const float* __restrict__ Delta,
     bf16* __restrict__ dQ, int N, int nqt, float scale, float scale_log2, int remap) {
@@ -398,16 +409,27 @@ hipError_t launch_pre(const BwdArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <int D, bool CAUSAL>
-hipError_t launch_dkdv(const BwdArgs& a, hipStream_t stream) {
+template <int D, bool CAUSAL, int OUT>
+hipError_t launch_dkdv_pass(const BwdArgs& a, hipStream_t stream) {
   const int nkt = (a.N + kBKV - 1) / kBKV;
   const uint32_t total = (uint32_t)a.B * a.H * nkt;
   const int remap = (total % 8u == 0u) ? 1 : 0;
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3(total), dim3(kThreads), 0, stream,
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, OUT>), dim3(total), dim3(kThreads), 0, stream,
                      (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, a.lse,
                      (const bf16*)a.dout, (const float*)a.delta, (bf16*)a.dk, (bf16*)a.dv, a.N, nkt,
                      a.scale, a.scale * kLog2e, remap);
   return hipGetLastError();
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch_dkdv(const BwdArgs& a, hipStream_t stream) {
+  if constexpr (D == 256) {  // two passes: dV, then dK
+    const hipError_t e = launch_dkdv_pass<D, CAUSAL, 1>(a, stream);
+    if (e != hipSuccess) return e;
+    return launch_dkdv_pass<D, CAUSAL, 2>(a, stream);
+  } else {
+    return launch_dkdv_pass<D, CAUSAL, 3>(a, stream);
+  }
 }
 
 template <int D, bool CAUSAL>
@@ -425,17 +447,23 @@ hipError_t launch_dq(const BwdArgs& a, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_bwd_pre(const BwdArgs& a, hipStream_t stream) {
-  return a.d == 64 ? launch_pre<64>(a, stream) : launch_pre<128>(a, stream);
+  if (a.d == 64) return launch_pre<64>(a, stream);
+  if (a.d == 256) return launch_pre<256>(a, stream);
+  return launch_pre<128>(a, stream);
 }
 
 hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t stream) {
   if (a.d == 64)
     return a.causal ? launch_dkdv<64, true>(a, stream) : launch_dkdv<64, false>(a, stream);
+  if (a.d == 256)
+    return a.causal ? launch_dkdv<256, true>(a, stream) : launch_dkdv<256, false>(a, stream);
   return a.causal ? launch_dkdv<128, true>(a, stream) : launch_dkdv<128, false>(a, stream);
 }
 
 hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t stream) {
   if (a.d == 64) return a.causal ? launch_dq<64, true>(a, stream) : launch_dq<64, false>(a, stream);
+  if (a.d == 256)
+    return a.causal ? launch_dq<256, true>(a, stream) : launch_dq<256, false>(a, stream);
   return a.causal ? launch_dq<128, true>(a, stream) : launch_dq<128, false>(a, stream);
 }
 

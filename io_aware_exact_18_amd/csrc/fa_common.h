@@ -105,11 +105,13 @@ __device__ inline float bf16_bits_to_float(uint32_t bits16) { return __uint_as_f
 //     once over any 16 consecutive rows;
 //   * transposed reads: 32 lanes read 4 consecutive rows × 64 bytes — the 4 rows' chunk groups land
 //     on disjoint bank quarters.
-// D = 128 (256-byte rows): H(r) = 4·(r mod 4) + (r/4 mod 4).
+// D = 128 (256-byte rows) and D = 256 (512-byte rows: the bank of chunk c is c mod 16, and H < 16
+// keeps c ^ H within its half-row): H(r) = 4·(r mod 4) + (r/4 mod 4).
 // D = 64 (128-byte rows, two rows per bank period): H(r) = 4·(r/2 mod 2) + (r/4 mod 4).
 template <int D>
 __device__ inline int swz_h(int r) {
-  if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
+  static_assert(D == 64 || D == 128 || D == 256, "head dimension");
+  if constexpr (D >= 128) return ((r & 3) << 2) | ((r >> 2) & 3);
   else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
 }
 template <int D>
@@ -120,22 +122,26 @@ __device__ inline int tile_off(int row, int col) {
 // Per-lane LDS byte offsets of the matrix-core fragments a lane reads from a tile in the tile_off<D>
 // layout.  H depends only on a row's low 4 bits, so a fragment 16 or 32 rows further down is the same
 // lane offset plus a compile-time constant (folded into the read's immediate offset).
+// With D = 256 the upper 256 bytes of a row repeat the lower half's chunk permutation (H < 16), so
+// a fragment there is the lower half's offset plus 256: only the first 128 columns' offsets are kept.
 template <int D>
 struct FragOffsets {
-  // Row read (16 bytes) of row 32kb + (lane % 32), d = 16s + 8g .. +7:  row[s] + 64·D·kb.
-  uint32_t row[D / 16];
+  static constexpr int DL = D < 128 ? D : 128;  // columns whose offsets are stored
+  // Row read (16 bytes) of row 32kb + (lane % 32), d = 16s + 8g .. +7:
+  // row[s % 8] + 256·(s / 8) + 64·D·kb.
+  uint32_t row[DL / 16];
   // Transposed read (8 bytes) of rows 16ks + 8h + 4g + tr_a, d = 32b + tr_n + 4 tr_b .. +3:
-  // tr[b][h] + 32·D·ks.
-  uint32_t tr[D / 32][2];
+  // tr[b % 4][h] + 256·(b / 4) + 32·D·ks.
+  uint32_t tr[DL / 32][2];
   __device__ explicit FragOffsets(int lane) {
     const int g = lane >> 5, lc = lane & 31;
     const int tr_a = (lane & 15) >> 2, tr_b = lane & 3, tr_n = 16 * ((lane >> 4) & 1);
 #pragma unroll
-    for (int s = 0; s < D / 16; ++s)
+    for (int s = 0; s < DL / 16; ++s)
       row[s] = (uint32_t)(lc * D * 2 + 16 * ((2 * s + g) ^ swz_h<D>(lc)));
     const int x = tr_n / 8 + (tr_b >> 1);
 #pragma unroll
-    for (int b = 0; b < D / 32; ++b)
+    for (int b = 0; b < DL / 32; ++b)
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const int r = 4 * g + tr_a + 8 * h;
@@ -147,15 +153,18 @@ struct FragOffsets {
 // A-/B-operand fragment with 8 consecutive d values: row 32kb + (lane % 32), d = 16s + 8g .. +7.
 template <int D>
 __device__ inline bf16x8 row_frag(const char* lds, const FragOffsets<D>& fo, int kb, int s) {
-  return *(const bf16x8*)(lds + fo.row[s] + kb * 64 * D);
+  constexpr int NS = FragOffsets<D>::DL / 16;
+  return *(const bf16x8*)(lds + fo.row[s % NS] + 256 * (s / NS) + kb * 64 * D);
 }
 
 // Operand fragment whose contraction index runs down the tile's rows: column d = 32b + (lane % 32),
 // slots e = 0..7 hold rows 16ks + 4g + 8(e/4) + (e%4).
 template <int D>
 __device__ inline bf16x8 tr_frag(const char* lds, const FragOffsets<D>& fo, int ks, int b) {
-  const u32x2 lo = lds_read_tr16((const bf16*)(lds + fo.tr[b][0] + ks * 32 * D));
-  const u32x2 hi = lds_read_tr16((const bf16*)(lds + fo.tr[b][1] + ks * 32 * D));
+  constexpr int NB = FragOffsets<D>::DL / 32;
+  const char* base = lds + 256 * (b / NB) + ks * 32 * D;
+  const u32x2 lo = lds_read_tr16((const bf16*)(base + fo.tr[b % NB][0]));
+  const u32x2 hi = lds_read_tr16((const bf16*)(base + fo.tr[b % NB][1]));
   const u32x4 v = {lo[0], lo[1], hi[0], hi[1]};
   return __builtin_bit_cast(bf16x8, v);
 }

@@ -73,7 +73,7 @@ __device__ inline void scores_tile(const char* klds, const FragOffsets<D>& fo,
 }
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
+__global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void fwd_bf16_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     bf16* __restrict__ O, float* __restrict__ LSE, int N, int nqt, float scale_log2, int remap) {
   constexpr int KSTEPS = D / 16;  // k-steps of the Sᵀ product
@@ -283,6 +283,7 @@ hipError_t launch(const FwdArgs& a, hipStream_t stream) {
 
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream) {
   if (a.d == 64) return a.causal ? launch<64, true>(a, stream) : launch<64, false>(a, stream);
+  if (a.d == 256) return a.causal ? launch<256, true>(a, stream) : launch<256, false>(a, stream);
   return a.causal ? launch<128, true>(a, stream) : launch<128, false>(a, stream);
 }
 

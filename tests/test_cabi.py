@@ -75,7 +75,8 @@ def test_fwd_rejections(lib):
     assert fwd(lib, N=0) == SHAPE
     assert fwd(lib, d=96) == UNSUP
     assert fwd(lib, d=32) == UNSUP
-    assert fwd(lib, d=256) == UNSUP
+    assert fwd(lib, d=512) == UNSUP
+    assert fwd8(lib, d=256) == UNSUP
     for bad in (0.0, -0.5, math.inf, math.nan):
         assert fwd(lib, scale=bad) == UNSUP
     assert fwd(lib, v=MIS) == ALIGN

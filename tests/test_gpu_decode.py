@@ -72,11 +72,12 @@ def _run(q, k, v, causal, scale, workspace=None):
 
 
 # Shapes: single key, ragged tiles (Nk not a multiple of 32), Nq up to 32, caches long enough to be
-# split into several chunks (≥ 512 keys with B·H = 2) with a ragged last chunk, both head dims.
+# split into several chunks (≥ 512 keys with B·H = 2) with a ragged last chunk, every head dim.
 SMALL = [
     (1, 1, 64, True), (1, 5, 128, False), (1, 33, 128, True), (3, 31, 64, True),
     (8, 64, 128, True), (8, 257, 128, True), (32, 32, 128, True), (32, 300, 64, False),
     (5, 1000, 128, True), (16, 3000, 128, True), (1, 4097, 64, False), (2, 777, 64, True),
+    (1, 1, 256, True), (7, 301, 256, True), (32, 1500, 256, False), (4, 2049, 256, True),
 ]
 
 

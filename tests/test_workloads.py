@@ -8,7 +8,9 @@ import workloads
 
 def test_workload_table():
     w = workloads.WORKLOADS
-    assert [x.number for x in w.values()] == [1, 2, 3, 4, 5]
+    assert [x.number for x in w.values()] == [1, 2, 3, 4, 5, 8]
+    assert w["d256_4k"].shape() == (4, 16, 4096, 256) and w["d256_4k"].causal
+    assert w["d256_4k"].fwd_flops() == w["causal_4k"].fwd_flops()
     assert w["causal_4k"].shape() == (4, 32, 4096, 128) and w["causal_4k"].causal
     # forward 4·B·H·N²·d halved when causal; backward 2.5× forward
     assert w["causal_4k"].fwd_flops() == 4 * 4 * 32 * 4096 ** 2 * 128 / 2
