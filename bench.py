@@ -284,8 +284,9 @@ def fp8_forward(fa, workloads, lib, steps, warmup):
 
 
 def fwd_bwd_secondary(fa, workloads, lib, name, steps, warmup):
-    """Secondary measurement: forward + backward of another bf16 workload (d256_4k: head dimension
-    256), each phase bracketed by events; TFLOP/s by the same FLOP convention as the headline."""
+    """Secondary measurement: forward + backward of another bf16 workload (d256_4k, d96_4k: head
+    dimensions 256 and 96), each phase bracketed by events; TFLOP/s by the same FLOP convention as
+    the headline."""
     import torch
     w = workloads.WORKLOADS[name]
     B, H, N, d = w.shape()
@@ -356,8 +357,9 @@ def main():
                     help="seconds of oracle work for the cpu_baseline leg (0 skips it)")
     ap.add_argument("--no-fp8", action="store_true",
                     help="skip the secondary FP8 forward measurement (fp8_8k workload)")
-    ap.add_argument("--no-d256", action="store_true",
-                    help="skip the secondary head-dimension-256 measurement (d256_4k workload)")
+    ap.add_argument("--no-head-dims", action="store_true",
+                    help="skip the secondary measurements at head dimensions 256 and 96 "
+                         "(d256_4k, d96_4k workloads)")
     ap.add_argument("--no-decode", action="store_true",
                     help="skip the secondary decoding measurements (decode_32k, specdec_32k)")
     ap.add_argument("--traffic-sweep", action="store_true",
@@ -504,9 +506,10 @@ def main():
     secondary = {}
     if not args.no_fp8:
         secondary["fp8_8k_fwd"] = fp8_forward(fa, workloads, lib, args.steps, args.warmup)
-    if not args.no_d256:
-        secondary["d256_4k_fwd_bwd"] = fwd_bwd_secondary(fa, workloads, lib, "d256_4k", args.steps,
-                                                         args.warmup)
+    if not args.no_head_dims:
+        for name in ("d256_4k", "d96_4k"):
+            secondary[name + "_fwd_bwd"] = fwd_bwd_secondary(fa, workloads, lib, name, args.steps,
+                                                             args.warmup)
     if not args.no_decode:
         secondary.update(decode_measure(fa, workloads, lib, args.steps, args.warmup))
 

@@ -18,7 +18,7 @@
  *  LSE        LSE_i = ln Σ_j exp(scale · q_i·k_j) over the keys query i may use: natural log of the
  *             scaled scores.  It stands for the pair (row maximum, softmax denominator).
  *  Causal     causal != 0 lets query i use key j only when j ≤ i; causal == 0 lets it use all keys.
- *  Supported  d ∈ {64, 128, 256} (fa_fwd_fp8: d = 128); N ≥ 1; B, H ≥ 1; B·H·N·d < 2^40.  bf16
+ *  Supported  d ∈ {64, 96, 128, 256} (fa_fwd_fp8: d = 128); N ≥ 1; B, H ≥ 1; B·H·N·d < 2^40.  bf16
  *             values are IEEE bfloat16.
  *  Memory     Every pointer is a device pointer owned by the caller and 16-byte aligned.  The library
  *             never allocates or frees device memory and keeps no state between calls.
@@ -42,7 +42,7 @@ typedef enum {
   FA_OK = 0,
   FA_ERR_NULL = 1,        /* a required pointer is NULL                                   */
   FA_ERR_SHAPE = 2,       /* B, H or N < 1, or the element count is out of range           */
-  FA_ERR_UNSUPPORTED = 3, /* d not in {64, 128, 256}, or a non-finite / non-positive scale */
+  FA_ERR_UNSUPPORTED = 3, /* d not in {64, 96, 128, 256}, or a bad scale / descale     */
   FA_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned                              */
   FA_ERR_WORKSPACE = 5,   /* backward workspace is NULL or smaller than fa_bwd_workspace_bytes */
   FA_ERR_LAUNCH = 6       /* the HIP runtime rejected a kernel launch                      */
@@ -131,7 +131,7 @@ fa_status fa_bwd_dq(const void* q, const void* k, const void* v, const float* ls
  *            into chunks attended to in parallel and merged by their softmax mass, the online-softmax
  *            recurrence of "Anatomy of a FlashAttention Kernel" applied to whole chunks) and needs no
  *            initialisation; its contents after the call are unspecified.
- *   d ∈ {64, 128, 256}; other conventions as above.  Results are deterministic.
+ *   d ∈ {64, 96, 128, 256}; other conventions as above.  Results are deterministic.
  *
  * Errors: FA_ERR_NULL (a tensor pointer is NULL), FA_ERR_SHAPE (B or H < 1, Nq outside [1, 32], Nk < Nq,
  * or the cache too large for 32-bit per-head offsets), FA_ERR_UNSUPPORTED (d, or a scale that is not

@@ -15,7 +15,7 @@ bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
 // (one extra tile of headroom), grids are 32-bit, and B·H·N·d stays below 2^40.
 fa_status check_shape(int B, int H, int N, int d, size_t elem_bytes) {
   if (B < 1 || H < 1 || N < 1) return FA_ERR_SHAPE;
-  if (d != 64 && d != 128 && d != 256) return FA_ERR_UNSUPPORTED;
+  if (d != 64 && d != 96 && d != 128 && d != 256) return FA_ERR_UNSUPPORTED;
   const uint64_t per_head = (uint64_t)(N + 256) * (uint64_t)d * elem_bytes;
   if (per_head >= (1ull << 31)) return FA_ERR_SHAPE;
   const uint64_t total = (uint64_t)B * (uint64_t)H * (uint64_t)N * (uint64_t)d;
@@ -173,7 +173,7 @@ fa_status fa_bwd_dq(const void* q, const void* k, const void* v, const float* ls
 
 size_t fa_decode_workspace_bytes(int B, int H, int Nq, int Nk, int d) {
   if (B < 1 || H < 1 || Nq < 1 || Nq > 32 || Nk < Nq) return 0;
-  if (d != 64 && d != 128 && d != 256) return 0;
+  if (d != 64 && d != 96 && d != 128 && d != 256) return 0;
   return fa::decode_workspace_bytes(B, H, Nq, Nk, d);
 }
 

@@ -38,22 +38,31 @@ constexpr int kBR = 128;   // dQ kernel: queries per workgroup (32 per wave)
 constexpr int kBC = 64;    // dQ kernel: keys per tile
 
 // ---------------------------------------------------------------------------------------------------
-// 1. D_i = Σ_t dO_it O_it.  One row per D/8 threads, 8 elements per thread.
+// 1. D_i = Σ_t dO_it O_it.  One row per pre_tpr<D>() threads (a power of two), each summing
+// D / (8·TPR) runs of 8 elements.
+template <int D>
+constexpr int pre_tpr() { return D == 96 ? 4 : D / 8; }
+
 template <int D>
 __global__ __launch_bounds__(kThreads) void bwd_pre_kernel(const bf16* __restrict__ O,
                                                            const bf16* __restrict__ dO,
                                                            float* __restrict__ delta, long rows) {
-  constexpr int TPR = D / 8;  // threads per row
+  constexpr int TPR = pre_tpr<D>();  // threads per row
+  constexpr int RUNS = D / (8 * TPR);
+  static_assert(RUNS * 8 * TPR == D && (TPR & (TPR - 1)) == 0, "row split");
   const long row = (long)blockIdx.x * (kThreads / TPR) + threadIdx.x / TPR;
   const int part = threadIdx.x % TPR;
   float acc = 0.f;
   if (row < rows) {
-    const u32x4 a = *(const u32x4*)(O + row * D + part * 8);
-    const u32x4 b = *(const u32x4*)(dO + row * D + part * 8);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      acc = fmaf(bf16_bits_to_float(a[i] & 0xffffu), bf16_bits_to_float(b[i] & 0xffffu), acc);
-      acc = fmaf(bf16_bits_to_float(a[i] >> 16), bf16_bits_to_float(b[i] >> 16), acc);
+    for (int u = 0; u < RUNS; ++u) {
+      const u32x4 a = *(const u32x4*)(O + row * D + (part * RUNS + u) * 8);
+      const u32x4 b = *(const u32x4*)(dO + row * D + (part * RUNS + u) * 8);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc = fmaf(bf16_bits_to_float(a[i] & 0xffffu), bf16_bits_to_float(b[i] & 0xffffu), acc);
+        acc = fmaf(bf16_bits_to_float(a[i] >> 16), bf16_bits_to_float(b[i] >> 16), acc);
+      }
     }
   }
 #pragma unroll
@@ -74,20 +83,21 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void bwd_dkdv_kernel(
     int remap) {
   constexpr int KSTEPS = D / 16;
   constexpr int DB = D / 32;
+  constexpr int L = lds_cols<D>();
   constexpr bool WANT_DV = (OUT & 1) != 0;
   constexpr bool WANT_DK = (OUT & 2) != 0;
-  // Q and dO tiles (tile_off<D> layout) and the tile's base-2 LSE and D values (first 32 of 64 used),
+  // Q and dO tiles (tile_off<L> layout) and the tile's base-2 LSE and D values (first 32 of 64 used),
   // double-buffered; separate LDS objects so reads of one buffer never wait for the LDS-DMA copy
   // filling the other.
-  __shared__ __attribute__((aligned(1024))) bf16 q0s[kBQ * D];
-  __shared__ __attribute__((aligned(1024))) bf16 q1s[kBQ * D];
-  __shared__ __attribute__((aligned(1024))) bf16 o0s[kBQ * D];
-  __shared__ __attribute__((aligned(1024))) bf16 o1s[kBQ * D];
+  __shared__ __attribute__((aligned(1024))) bf16 q0s[kBQ * L];
+  __shared__ __attribute__((aligned(1024))) bf16 q1s[kBQ * L];
+  __shared__ __attribute__((aligned(1024))) bf16 o0s[kBQ * L];
+  __shared__ __attribute__((aligned(1024))) bf16 o1s[kBQ * L];
   __shared__ __attribute__((aligned(256))) float l0s[64];
   __shared__ __attribute__((aligned(256))) float l1s[64];
   __shared__ __attribute__((aligned(256))) float d0s[64];
   __shared__ __attribute__((aligned(256))) float d1s[64];
-  __shared__ __attribute__((aligned(1024))) bf16 vts[WANT_DK ? kBKV * D : 8];  // the workgroup's V rows
+  __shared__ __attribute__((aligned(1024))) bf16 vts[WANT_DK ? kBKV * L : 8];  // the workgroup's V rows
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -123,7 +133,7 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void bwd_dkdv_kernel(
     copy_v(make_rsrc(V + head, head_bytes), k0, vts);
   }
 
-  const FragOffsets<D> fo(lane);
+  const FragOffsets<L> fo(lane);
   const int qstart = CAUSAL ? k0 : 0;  // causal: only queries ≥ the tile's first key
   const int nsteps = (N - qstart + kBQ - 1) / kBQ;
 
@@ -174,9 +184,9 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void bwd_dkdv_kernel(
       }
 #pragma unroll
       for (int s = 0; s < KSTEPS; ++s) {
-        sacc = mfma_32x32x16(row_frag<D>(qs, fo, 0, s), kf[s], sacc);
+        sacc = mfma_32x32x16(row_frag<L>(qs, fo, 0, s), kf[s], sacc);
         if constexpr (WANT_DK)
-          pacc = mfma_32x32x16(row_frag<D>(dos, fo, 0, s), row_frag<D>((const char*)vts, fo, wave, s),
+          pacc = mfma_32x32x16(row_frag<L>(dos, fo, 0, s), row_frag<L>((const char*)vts, fo, wave, s),
                                pacc);
       }
       // Element r: query qb + 8(r/4) + 4g + (r%4), key kj.  Masked scores become -inf (P = 0) in a
@@ -213,8 +223,8 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void bwd_dkdv_kernel(
       for (int b = 0; b < DB; ++b) {
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-          if constexpr (WANT_DV) dva[b] = mfma_32x32x16(tr_frag<D>(dos, fo, ks, b), pb[ks], dva[b]);
-          if constexpr (WANT_DK) dka[b] = mfma_32x32x16(tr_frag<D>(qs, fo, ks, b), dsb[ks], dka[b]);
+          if constexpr (WANT_DV) dva[b] = mfma_32x32x16(tr_frag<L>(dos, fo, ks, b), pb[ks], dva[b]);
+          if constexpr (WANT_DK) dka[b] = mfma_32x32x16(tr_frag<L>(qs, fo, ks, b), dsb[ks], dka[b]);
         }
       }
     }
@@ -261,12 +271,13 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void bwd_dq_kernel(
     bf16* __restrict__ dQ, int N, int nqt, float scale, float scale_log2, int remap) {
   constexpr int KSTEPS = D / 16;
   constexpr int DB = D / 32;
-  // K and V tiles (tile_off<D> layout), double-buffered, as separate LDS objects (see the dK/dV
+  constexpr int L = lds_cols<D>();
+  // K and V tiles (tile_off<L> layout), double-buffered, as separate LDS objects (see the dK/dV
   // kernel).
-  __shared__ __attribute__((aligned(1024))) bf16 k0s[kBC * D];
-  __shared__ __attribute__((aligned(1024))) bf16 k1s[kBC * D];
-  __shared__ __attribute__((aligned(1024))) bf16 v0s[kBC * D];
-  __shared__ __attribute__((aligned(1024))) bf16 v1s[kBC * D];
+  __shared__ __attribute__((aligned(1024))) bf16 k0s[kBC * L];
+  __shared__ __attribute__((aligned(1024))) bf16 k1s[kBC * L];
+  __shared__ __attribute__((aligned(1024))) bf16 v0s[kBC * L];
+  __shared__ __attribute__((aligned(1024))) bf16 v1s[kBC * L];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -305,7 +316,7 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void bwd_dq_kernel(
 
   const int kv_end = CAUSAL ? min(N, q0 + kBR) : N;
   const int ntiles = (kv_end + kBC - 1) / kBC;
-  const FragOffsets<D> fo(lane);
+  const FragOffsets<L> fo(lane);
 
   f32x16 qacc[DB];  // dQᵀ: rows d = 32b + 8(r/4) + 4g + r%4, column = this lane's query
 #pragma unroll
@@ -342,8 +353,8 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void bwd_dq_kernel(
       for (int s = 0; s < KSTEPS; ++s)
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
-          sacc[kb] = mfma_32x32x16(row_frag<D>(klds, fo, kb, s), qf[s], sacc[kb]);
-          pacc[kb] = mfma_32x32x16(row_frag<D>(vlds, fo, kb, s), df[s], pacc[kb]);
+          sacc[kb] = mfma_32x32x16(row_frag<L>(klds, fo, kb, s), qf[s], sacc[kb]);
+          pacc[kb] = mfma_32x32x16(row_frag<L>(vlds, fo, kb, s), df[s], pacc[kb]);
         }
       // Masked scores become -inf (P = 0) in a wave-uniform branch taken only by diagonal and
       // ragged tiles.
@@ -374,7 +385,7 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void bwd_dq_kernel(
       for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
         for (int b = 0; b < DB; ++b)
-          qacc[b] = mfma_32x32x16(tr_frag<D>(klds, fo, ks, b), dsf[ks], qacc[b]);
+          qacc[b] = mfma_32x32x16(tr_frag<L>(klds, fo, ks, b), dsf[ks], qacc[b]);
     }
     wait_vmem_all();
     __syncthreads();
@@ -402,7 +413,7 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void bwd_dq_kernel(
 template <int D>
 hipError_t launch_pre(const BwdArgs& a, hipStream_t stream) {
   const long rows = (long)a.B * a.H * a.N;
-  constexpr int rows_per_block = kThreads / (D / 8);
+  constexpr int rows_per_block = kThreads / pre_tpr<D>();
   hipLaunchKernelGGL((bwd_pre_kernel<D>),
                      dim3((unsigned)((rows + rows_per_block - 1) / rows_per_block)),
                      dim3(kThreads), 0, stream, (const bf16*)a.o, (const bf16*)a.dout, a.delta, rows);
@@ -448,6 +459,7 @@ hipError_t launch_dq(const BwdArgs& a, hipStream_t stream) {
 
 hipError_t launch_bwd_pre(const BwdArgs& a, hipStream_t stream) {
   if (a.d == 64) return launch_pre<64>(a, stream);
+  if (a.d == 96) return launch_pre<96>(a, stream);
   if (a.d == 256) return launch_pre<256>(a, stream);
   return launch_pre<128>(a, stream);
 }
@@ -455,6 +467,8 @@ hipError_t launch_bwd_pre(const BwdArgs& a, hipStream_t stream) {
 hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t stream) {
   if (a.d == 64)
     return a.causal ? launch_dkdv<64, true>(a, stream) : launch_dkdv<64, false>(a, stream);
+  if (a.d == 96)
+    return a.causal ? launch_dkdv<96, true>(a, stream) : launch_dkdv<96, false>(a, stream);
   if (a.d == 256)
     return a.causal ? launch_dkdv<256, true>(a, stream) : launch_dkdv<256, false>(a, stream);
   return a.causal ? launch_dkdv<128, true>(a, stream) : launch_dkdv<128, false>(a, stream);
@@ -462,6 +476,7 @@ hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t stream) {
 
 hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t stream) {
   if (a.d == 64) return a.causal ? launch_dq<64, true>(a, stream) : launch_dq<64, false>(a, stream);
+  if (a.d == 96) return a.causal ? launch_dq<96, true>(a, stream) : launch_dq<96, false>(a, stream);
   if (a.d == 256)
     return a.causal ? launch_dq<256, true>(a, stream) : launch_dq<256, false>(a, stream);
   return a.causal ? launch_dq<128, true>(a, stream) : launch_dq<128, false>(a, stream);

@@ -114,6 +114,15 @@ __device__ inline int swz_h(int r) {
   if constexpr (D >= 128) return ((r & 3) << 2) | ((r >> 2) & 3);
   else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
 }
+// Columns of the LDS layout of a tile whose rows hold D values: D = 96 is kept in the D = 128 layout
+// (256-byte rows; the last 32 columns are zero-filled by the copy and never read), so the swizzle
+// and fragment offsets of D = 128 apply unchanged.
+template <int D>
+constexpr int lds_cols() {
+  static_assert(D == 64 || D == 96 || D == 128 || D == 256, "head dimension");
+  return D == 96 ? 128 : D;
+}
+
 template <int D>
 __device__ inline int tile_off(int row, int col) {
   return row * D + ((((col >> 3) ^ swz_h<D>(row)) << 3) | (col & 7));
@@ -169,18 +178,24 @@ __device__ inline bf16x8 tr_frag(const char* lds, const FragOffsets<D>& fo, int 
   return __builtin_bit_cast(bf16x8, v);
 }
 
-// Asynchronous copy of ROWS rows of ROW_BYTES bytes (rows row0 .. row0+ROWS-1 of the matrix behind
-// the buffer resource `r`) into LDS by NT threads, without passing through registers
-// (buffer_load_dwordx4 ... lds: lane i of a wave writes LDS bytes [16 i, 16 i + 16) after the
-// wave-uniform base).  Rows past the buffer's end read as zeros.  The 16-byte chunk c of row r is
+// Asynchronous copy of ROWS rows (rows row0 .. row0+ROWS-1 of the matrix behind the buffer resource
+// `r`, GROW_BYTES bytes apart) into LDS rows of ROW_BYTES ≥ GROW_BYTES bytes by NT threads, without
+// passing through registers (buffer_load_dwordx4 ... lds: lane i of a wave writes LDS bytes
+// [16 i, 16 i + 16) after the wave-uniform base).  Rows past the buffer's end read as zeros, and so
+// do the LDS chunks past GROW_BYTES (their source offset is set beyond any buffer's range, so they
+// cost no memory traffic).  The 16-byte chunk c of row r is
 // stored at physical chunk c ^ swz(r), where swz depends only on r mod 16.  An issue round covers
 // NT / (ROW_BYTES / 16) rows; the swizzle repeats every 16 rows, so a lane's offset within a round
 // takes PAT = max(1, 16 / rows-per-round) values, computed once, here, and each load of a copy adds
 // a scalar row offset to one of them (one vector add; the row offset stays in the range-checked
 // vector offset so the zero fill of ragged tails still applies).  Completion: wait_vmem_all().
-template <int ROW_BYTES, int ROWS, int NT>
+template <int ROW_BYTES, int ROWS, int NT, int GROW_BYTES = ROW_BYTES>
 struct TileCopy {
   static constexpr int CPR = ROW_BYTES / 16;        // 16-byte chunks per row
+  static_assert(GROW_BYTES % 16 == 0 && GROW_BYTES <= ROW_BYTES, "source rows of whole chunks");
+  // Source offset of a padding chunk: at least 2^31, past every buffer's range (heads are < 2 GiB),
+  // and still below 2^32 after a row offset (< 2^31) is added.
+  static constexpr uint32_t kPad = 0x80000000u;
   static constexpr int ROUNDS = ROWS * CPR / NT;    // loads per thread
   static constexpr int ROUND_ROWS = NT / CPR;       // rows per round
   static constexpr int PAT = ROUND_ROWS >= 16 ? 1 : 16 / ROUND_ROWS;  // distinct lane offsets
@@ -197,14 +212,15 @@ struct TileCopy {
 #pragma unroll
     for (int p = 0; p < PAT; ++p) {
       const int row = p * ROUND_ROWS + slot / CPR;
-      voff[p] = (uint32_t)(row * ROW_BYTES + 16 * (pc ^ swz(row)));  // logical chunk held by slot pc
+      const int c = pc ^ swz(row);  // logical chunk held by slot pc
+      voff[p] = 16 * c < GROW_BYTES ? (uint32_t)(row * GROW_BYTES + 16 * c) : kPad;
     }
   }
   template <class T>
   __device__ void operator()(__amdgpu_buffer_rsrc_t r, int row0, T* lds) const {
 #pragma unroll
     for (int i = 0; i < ROUNDS; ++i) {
-      const uint32_t base = (uint32_t)(row0 + (i / PAT) * PAT * ROUND_ROWS) * (uint32_t)ROW_BYTES;
+      const uint32_t base = (uint32_t)(row0 + (i / PAT) * PAT * ROUND_ROWS) * (uint32_t)GROW_BYTES;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           r, (__attribute__((address_space(3))) void*)((char*)lds + (i * (NT / 64) + wave) * 1024),
           16, (uint32_t)(voff[i % PAT] + base), 0, 0, 0);
@@ -212,11 +228,12 @@ struct TileCopy {
   }
 };
 
-// TileCopy for a [ROWS][D] bf16 tile in the tile_off<D> layout.
+// TileCopy for a [ROWS][D] bf16 tile into the tile_off<lds_cols<D>()> layout.
 template <int D, int ROWS, int NT>
-struct BfTileCopy : TileCopy<2 * D, ROWS, NT> {
+struct BfTileCopy : TileCopy<2 * lds_cols<D>(), ROWS, NT, 2 * D> {
   __device__ explicit BfTileCopy(int tid)
-      : TileCopy<2 * D, ROWS, NT>(tid, [](int r) { return swz_h<D>(r); }) {}
+      : TileCopy<2 * lds_cols<D>(), ROWS, NT, 2 * D>(tid,
+                                                     [](int r) { return swz_h<lds_cols<D>()>(r); }) {}
 };
 
 // Asynchronous copy of 64 consecutive fp32 values (elements e0 .. e0+63 behind `r`) into LDS by one

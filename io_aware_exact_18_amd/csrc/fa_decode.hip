@@ -39,13 +39,14 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
     float scale_log2) {
   constexpr int KSTEPS = D / 16;
   constexpr int DB = D / 32;
+  constexpr int L = lds_cols<D>();
   // K/V tiles, double-buffered (separate LDS objects, so reads of one buffer never wait for the DMA
   // filling the other): tile j lives in buffers j % 2.  Deeper rings (3 or 4 tiles) measured the same:
   // the call already streams the cache at the device's achievable read rate.
-  __shared__ __attribute__((aligned(1024))) bf16 k0s[kDecBC * D];
-  __shared__ __attribute__((aligned(1024))) bf16 k1s[kDecBC * D];
-  __shared__ __attribute__((aligned(1024))) bf16 v0s[kDecBC * D];
-  __shared__ __attribute__((aligned(1024))) bf16 v1s[kDecBC * D];
+  __shared__ __attribute__((aligned(1024))) bf16 k0s[kDecBC * L];
+  __shared__ __attribute__((aligned(1024))) bf16 k1s[kDecBC * L];
+  __shared__ __attribute__((aligned(1024))) bf16 v0s[kDecBC * L];
+  __shared__ __attribute__((aligned(1024))) bf16 v1s[kDecBC * L];
 
   const int lane = threadIdx.x;
   const int g = lane >> 5;
@@ -62,7 +63,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
   const auto rq = make_rsrc(Q + (size_t)bh * Nq * D, (uint32_t)Nq * D * 2u);  // rows ≥ Nq read 0
   const auto rk = make_rsrc(K + kv_head, kv_bytes);
   const auto rv = make_rsrc(V + kv_head, kv_bytes);
-  const TileCopy<2 * D, kDecBC, kDecThreads> copy(lane, [](int r) { return swz_h<D>(r); });
+  const BfTileCopy<D, kDecBC, kDecThreads> copy(lane);
 
   bf16x8 qf[KSTEPS];  // Qᵀ fragments (B operand): column = this lane's query, d = 16s + 8g .. +7
 #pragma unroll
@@ -70,7 +71,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
     qf[s] = __builtin_bit_cast(bf16x8, buf_load16(rq, (uint32_t)(lc * D + 16 * s + 8 * g) * 2u));
 
   const int ntiles = (k_end - k_begin + kDecBC - 1) / kDecBC;
-  const FragOffsets<D> fo(lane);
+  const FragOffsets<L> fo(lane);
   copy(rk, k_begin, k0s);
   copy(rv, k_begin, v0s);
 
@@ -99,7 +100,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
 #pragma unroll
     for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
 #pragma unroll
-    for (int s = 0; s < KSTEPS; ++s) sacc = mfma_32x32x16(row_frag<D>(klds, fo, 0, s), qf[s], sacc);
+    for (int s = 0; s < KSTEPS; ++s) sacc = mfma_32x32x16(row_frag<L>(klds, fo, 0, s), qf[s], sacc);
     // Keys past the chunk (the last tile may be ragged) and, causal, past the query's position.
     if ((kv0 + kDecBC > k_end) || (CAUSAL && kv0 + kDecBC - 1 > q_first_pos)) {
 #pragma unroll
@@ -138,7 +139,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
     for (int ks = 0; ks < 2; ++ks) {
       bf16x8 vf[DB];
 #pragma unroll
-      for (int b = 0; b < DB; ++b) vf[b] = tr_frag<D>(vlds, fo, ks, b);
+      for (int b = 0; b < DB; ++b) vf[b] = tr_frag<L>(vlds, fo, ks, b);
 #pragma unroll
       for (int b = 0; b < DB; ++b) oacc[b] = mfma_32x32x16(vf[b], pf[ks], oacc[b]);
     }
@@ -178,7 +179,7 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(const float* __restric
                                                           const float* __restrict__ part_ml,
                                                           bf16* __restrict__ O,
                                                           float* __restrict__ LSE, int Nq, int S) {
-  constexpr int PER = D / 64;
+  constexpr int PER = (D + 63) / 64;  // values per lane (the last partly idle when D = 96)
   const int lane = threadIdx.x;
   const int bh = blockIdx.x / Nq;
   const int qi = blockIdx.x % Nq;
@@ -194,12 +195,14 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(const float* __restric
     const float w = exp2_fast(ms - m);  // 0 for a chunk without usable keys (ms = -inf)
     l += w * part_ml[2 * row + 1];
 #pragma unroll
-    for (int t = 0; t < PER; ++t) acc[t] += w * part_o[row * D + lane + 64 * t];
+    for (int t = 0; t < PER; ++t)
+      if (D % 64 == 0 || lane + 64 * t < D) acc[t] += w * part_o[row * D + lane + 64 * t];
   }
   const float inv = 1.f / l;
   const size_t orow = ((size_t)bh * Nq + qi) * D;
 #pragma unroll
-  for (int t = 0; t < PER; ++t) O[orow + lane + 64 * t] = (__bf16)(acc[t] * inv);
+  for (int t = 0; t < PER; ++t)
+    if (D % 64 == 0 || lane + 64 * t < D) O[orow + lane + 64 * t] = (__bf16)(acc[t] * inv);
   if (lane == 0) LSE[(size_t)bh * Nq + qi] = (m + __log2f(l)) * kLn2;
 }
 
@@ -223,6 +226,7 @@ hipError_t launch(const DecodeArgs& a, hipStream_t stream) {
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
   if (a.d == 64) return a.causal ? launch<64, true>(a, stream) : launch<64, false>(a, stream);
+  if (a.d == 96) return a.causal ? launch<96, true>(a, stream) : launch<96, false>(a, stream);
   if (a.d == 256) return a.causal ? launch<256, true>(a, stream) : launch<256, false>(a, stream);
   return a.causal ? launch<128, true>(a, stream) : launch<128, false>(a, stream);
 }

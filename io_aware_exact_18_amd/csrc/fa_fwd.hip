@@ -58,7 +58,7 @@ __device__ inline T& pick(T& a, T& b) {
 // query = this lane's query.  The two key blocks' chains are interleaved and each K fragment is read
 // two products ahead of its use.
 template <int D>
-__device__ inline void scores_tile(const char* klds, const FragOffsets<D>& fo,
+__device__ inline void scores_tile(const char* klds, const FragOffsets<lds_cols<D>()>& fo,
                                    const bf16x8 (&qf)[D / 16], f32x16 (&acc)[2]) {
   constexpr int NS = D / 16;
 #pragma unroll
@@ -67,7 +67,7 @@ __device__ inline void scores_tile(const char* klds, const FragOffsets<D>& fo,
     for (int r = 0; r < 16; ++r) acc[kb][r] = 0.f;
   bf16x8 f[2 * NS];
 #pragma unroll
-  for (int i = 0; i < 2 * NS; ++i) f[i] = row_frag<D>(klds, fo, i & 1, i >> 1);
+  for (int i = 0; i < 2 * NS; ++i) f[i] = row_frag<lds_cols<D>()>(klds, fo, i & 1, i >> 1);
 #pragma unroll
   for (int i = 0; i < 2 * NS; ++i) acc[i & 1] = mfma_32x32x16(f[i], qf[i >> 1], acc[i & 1]);
 }
@@ -78,13 +78,14 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void fwd_bf16_kernel(
     bf16* __restrict__ O, float* __restrict__ LSE, int N, int nqt, float scale_log2, int remap) {
   constexpr int KSTEPS = D / 16;  // k-steps of the Sᵀ product
   constexpr int DB = D / 32;      // 32-row blocks of Oᵀ
-  // K(j) lives in k<j % 2>, V(j) in v<j % 2> (tile_off<D> layout).  Four separate LDS objects, so the
+  constexpr int L = lds_cols<D>();
+  // K(j) lives in k<j % 2>, V(j) in v<j % 2> (tile_off<L> layout).  Four separate LDS objects, so the
   // compiler can tell the buffer being read from the one an in-flight LDS-DMA copy is writing and
   // does not wait for the copy before unrelated reads.
-  __shared__ __attribute__((aligned(1024))) bf16 k0s[kBC * D];
-  __shared__ __attribute__((aligned(1024))) bf16 k1s[kBC * D];
-  __shared__ __attribute__((aligned(1024))) bf16 v0s[kBC * D];
-  __shared__ __attribute__((aligned(1024))) bf16 v1s[kBC * D];
+  __shared__ __attribute__((aligned(1024))) bf16 k0s[kBC * L];
+  __shared__ __attribute__((aligned(1024))) bf16 k1s[kBC * L];
+  __shared__ __attribute__((aligned(1024))) bf16 v0s[kBC * L];
+  __shared__ __attribute__((aligned(1024))) bf16 v1s[kBC * L];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -118,7 +119,7 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void fwd_bf16_kernel(
   const int ntiles = (kv_end + kBC - 1) / kBC;
   // Tiles at or beyond this index are fully masked for this wave (causal): no math on them.
   const int wave_tiles = CAUSAL ? min(ntiles, (qw + 31) / kBC + 1) : ntiles;
-  const FragOffsets<D> fo(lane);
+  const FragOffsets<L> fo(lane);
 
   // Prologue: K(0), K(1), V(0) in flight; scores of tile 0.
   copy(mk, 0, k0s);
@@ -223,7 +224,7 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void fwd_bf16_kernel(
       for (int ks = 0; ks < 4; ++ks) {
         bf16x8 vf[DB];
 #pragma unroll
-        for (int b = 0; b < DB; ++b) vf[b] = tr_frag<D>(vlds, fo, ks, b);
+        for (int b = 0; b < DB; ++b) vf[b] = tr_frag<L>(vlds, fo, ks, b);
 #pragma unroll
         for (int b = 0; b < DB; ++b) oacc[b] = mfma_32x32x16(vf[b], pf[ks], oacc[b]);
       }
@@ -283,6 +284,7 @@ hipError_t launch(const FwdArgs& a, hipStream_t stream) {
 
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream) {
   if (a.d == 64) return a.causal ? launch<64, true>(a, stream) : launch<64, false>(a, stream);
+  if (a.d == 96) return a.causal ? launch<96, true>(a, stream) : launch<96, false>(a, stream);
   if (a.d == 256) return a.causal ? launch<256, true>(a, stream) : launch<256, false>(a, stream);
   return a.causal ? launch<128, true>(a, stream) : launch<128, false>(a, stream);
 }

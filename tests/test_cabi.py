@@ -73,7 +73,8 @@ def test_fwd_rejections(lib):
     assert fwd(lib, B=0) == SHAPE
     assert fwd(lib, H=-1) == SHAPE
     assert fwd(lib, N=0) == SHAPE
-    assert fwd(lib, d=96) == UNSUP
+    assert fwd(lib, d=80) == UNSUP
+    assert fwd8(lib, d=96) == UNSUP
     assert fwd(lib, d=32) == UNSUP
     assert fwd(lib, d=512) == UNSUP
     assert fwd8(lib, d=256) == UNSUP
@@ -103,7 +104,8 @@ def test_workspace_bytes(lib):
         return (x + 255) // 256 * 256
     for B, H, N, d in ((1, 1, 1, 64), (8, 16, 2048, 64), (4, 32, 4096, 128), (1, 3, 17, 128)):
         assert lib.fa_bwd_workspace_bytes(B, H, N, d) == up(B * H * N * 4)
-    assert lib.fa_bwd_workspace_bytes(1, 1, 64, 96) == 0
+    assert lib.fa_bwd_workspace_bytes(1, 1, 64, 96) == 256
+    assert lib.fa_bwd_workspace_bytes(1, 1, 64, 80) == 0
     assert lib.fa_bwd_workspace_bytes(0, 1, 64, 64) == 0
 
 
@@ -163,13 +165,14 @@ def _decode_split(B, H, Nk):
 
 def test_decode_workspace_formula(lib):
     for B, H, Nq, Nk, d in ((1, 1, 1, 1, 64), (4, 32, 1, 32768, 128), (4, 32, 8, 32768, 128),
-                            (1, 2, 3, 3000, 64), (2, 3, 32, 257, 128), (64, 64, 4, 100, 128)):
+                            (1, 2, 3, 3000, 64), (2, 3, 32, 257, 128), (64, 64, 4, 100, 128),
+                            (1, 2, 5, 999, 96), (2, 2, 4, 4096, 256)):
         S, length = _decode_split(B, H, Nk)
         assert (S - 1) * length < Nk <= S * length
         want = -(-(B * H * S * Nq * (d + 2) * 4) // 256) * 256
         assert lib.fa_decode_workspace_bytes(B, H, Nq, Nk, d) == want, (B, H, Nq, Nk, d)
     for bad in ((0, 1, 1, 8, 64), (1, 1, 0, 8, 64), (1, 1, 33, 64, 64), (1, 1, 9, 8, 64),
-                (1, 1, 1, 8, 96)):
+                (1, 1, 1, 8, 80), (1, 1, 1, 8, 512)):
         assert lib.fa_decode_workspace_bytes(*bad) == 0, bad
 
 
@@ -186,7 +189,7 @@ def test_decode_rejections(lib):
     assert decode(lib, Nq=9, Nk=8) == SHAPE
     assert decode(lib, B=0) == SHAPE
     assert decode(lib, Nk=1 << 23, d=128) == SHAPE  # per-head cache past 32-bit offsets
-    assert decode(lib, d=96) == UNSUP
+    assert decode(lib, d=80) == UNSUP
     assert decode(lib, scale=0.0) == UNSUP
     assert decode(lib, scale=math.inf) == UNSUP
     assert decode(lib, ws=None) == WORKSPACE

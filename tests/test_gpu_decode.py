@@ -78,6 +78,7 @@ SMALL = [
     (8, 64, 128, True), (8, 257, 128, True), (32, 32, 128, True), (32, 300, 64, False),
     (5, 1000, 128, True), (16, 3000, 128, True), (1, 4097, 64, False), (2, 777, 64, True),
     (1, 1, 256, True), (7, 301, 256, True), (32, 1500, 256, False), (4, 2049, 256, True),
+    (1, 1, 96, True), (3, 333, 96, False), (32, 1024, 96, True), (8, 2500, 96, True),
 ]
 
 

@@ -182,7 +182,7 @@ def test_fp8_rising_row_maximum(step_log2, causal):
 # ------------------------------------------------------------------------------------------------
 # Forward, small and ragged shapes.
 
-SMALL = [(1, 2, n, d, c) for d in (64, 128, 256) for c in (False, True)
+SMALL = [(1, 2, n, d, c) for d in (64, 96, 128, 256) for c in (False, True)
          for n in (1, 17, 64, 100, 129, 256, 300)]
 
 
@@ -195,7 +195,7 @@ def test_fwd_small(B, H, N, d, causal):
     _check_fwd_heads(q, k, v, o.cpu(), lse.cpu(), causal, scale)
 
 
-@pytest.mark.parametrize("d", [64, 128, 256])
+@pytest.mark.parametrize("d", [64, 96, 128, 256])
 @pytest.mark.parametrize("causal", [False, True])
 def test_fwd_equal_scores_closed_form(d, causal):
     """Q = 0: O_i is the mean of the allowed V rows and LSE_i = ln(#allowed keys)."""
@@ -215,7 +215,7 @@ def test_fwd_equal_scores_closed_form(d, causal):
     assert (lse.cpu().double() - lref).abs().max().item() <= 1e-5
 
 
-@pytest.mark.parametrize("d", [64, 128, 256])
+@pytest.mark.parametrize("d", [64, 96, 128, 256])
 def test_fwd_causal_row0_exact(d):
     """Under the causal mask row 0 sees only key 0: O_0 = V_0 exactly, LSE_0 = scale·q_0·k_0."""
     g = torch.Generator().manual_seed(11)
@@ -227,7 +227,7 @@ def test_fwd_causal_row0_exact(d):
     assert (lse[:, :, 0].cpu().double() - ref).abs().max().item() <= 1e-5
 
 
-@pytest.mark.parametrize("d", [128, 256])
+@pytest.mark.parametrize("d", [96, 128, 256])
 def test_fwd_deterministic_and_guarded(d):
     """Two runs are bitwise equal, and nothing is written past the end of O or LSE."""
     B, H, N = 2, 3, 333
@@ -252,7 +252,7 @@ def test_fwd_deterministic_and_guarded(d):
 # ------------------------------------------------------------------------------------------------
 # Backward, small and ragged shapes.
 
-SMALL_BWD = [(1, 2, n, d, c) for d in (64, 128, 256) for c in (False, True)
+SMALL_BWD = [(1, 2, n, d, c) for d in (64, 96, 128, 256) for c in (False, True)
              for n in (1, 17, 100, 129, 256, 300)]
 
 
@@ -268,12 +268,13 @@ def test_bwd_small(B, H, N, d, causal):
     _check_bwd_heads(q, k, v, do, dq.cpu(), dk.cpu(), dv.cpu(), causal, scale, range(B * H))
 
 
+@pytest.mark.parametrize("d", [96, 256])
 @pytest.mark.parametrize("causal", [False, True])
-def test_d256_many_tiles(causal):
-    """Head dimension 256 over many key and query tiles with a ragged tail (N = 1100), forward and
-    backward, every head against the oracle."""
-    B, H, N, d = 1, 2, 1100, 256
-    g = torch.Generator().manual_seed(256 + int(causal))
+def test_wide_heads_many_tiles(d, causal):
+    """Head dimensions 96 and 256 over many key and query tiles with a ragged tail (N = 1100),
+    forward and backward, every head against the oracle."""
+    B, H, N = 1, 2, 1100
+    g = torch.Generator().manual_seed(d + int(causal))
     q, k, v, do = (torch.randn(B, H, N, d, generator=g).to(torch.bfloat16) for _ in range(4))
     scale = 1.0 / math.sqrt(d)
     o, lse, dq, dk, dv = _run_bwd(q, k, v, do, causal, scale)
@@ -281,7 +282,7 @@ def test_d256_many_tiles(causal):
     _check_bwd_heads(q, k, v, do, dq.cpu(), dk.cpu(), dv.cpu(), causal, scale, range(B * H))
 
 
-@pytest.mark.parametrize("d", [128, 256])
+@pytest.mark.parametrize("d", [96, 128, 256])
 def test_bwd_guarded(d):
     """Nothing is written past dQ, dK, dV or the workspace's documented size."""
     B, H, N = 1, 2, 190
@@ -320,7 +321,7 @@ def test_workload_fwd_small_full():
     _check_fwd_heads(inp["q"], inp["k"], inp["v"], o.cpu(), lse.cpu(), w.causal, w.scale)
 
 
-@pytest.mark.parametrize("name", ["d64_2k", "causal_4k", "long_16k", "d256_4k"])
+@pytest.mark.parametrize("name", ["d64_2k", "causal_4k", "long_16k", "d256_4k", "d96_4k"])
 def test_workload_reduced(name):
     """Each backward workload at its own N and d but only 2 heads: every head checked."""
     w = workloads.WORKLOADS[name]
@@ -334,7 +335,7 @@ def test_workload_reduced(name):
                      w.causal, w.scale, heads)
 
 
-@pytest.mark.parametrize("name", ["d64_2k", "causal_4k", "d256_4k"])
+@pytest.mark.parametrize("name", ["d64_2k", "causal_4k", "d256_4k", "d96_4k"])
 def test_workload_full(name):
     """Full size, as the bench runs it: sampled heads against the oracle, properties on all heads."""
     w = workloads.WORKLOADS[name]
@@ -374,7 +375,7 @@ def test_workload_long_full():
     _check_bwd_sums(inp["do"], dk, dv)
 
 
-@pytest.mark.parametrize("d", [128, 256])
+@pytest.mark.parametrize("d", [96, 128, 256])
 def test_bwd_phases_equal_fused_call(d):
     """fa_bwd_preprocess + fa_bwd_dkdv + fa_bwd_dq give bitwise what fa_bwd gives, and fa_bwd is
     deterministic from run to run."""

@@ -8,7 +8,8 @@ import workloads
 
 def test_workload_table():
     w = workloads.WORKLOADS
-    assert [x.number for x in w.values()] == [1, 2, 3, 4, 5, 8]
+    assert [x.number for x in w.values()] == [1, 2, 3, 4, 5, 8, 9]
+    assert w["d96_4k"].shape() == (4, 32, 4096, 96)
     assert w["d256_4k"].shape() == (4, 16, 4096, 256) and w["d256_4k"].causal
     assert w["d256_4k"].fwd_flops() == w["causal_4k"].fwd_flops()
     assert w["causal_4k"].shape() == (4, 32, 4096, 128) and w["causal_4k"].causal

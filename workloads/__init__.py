@@ -17,6 +17,7 @@ long_16k  1, 32, 16384, 128      yes     forward + backward, bf16, one ×8 key p
 fp8_8k    4, 32, 8192, 128       yes     forward only, e4m3 Q/K/V with per-tensor scales, O bf16
 d256_4k   4, 16, 4096, 256       yes     forward + backward, bf16, head dimension 256 (the FLOPs of
                                          causal_4k with half the heads, each twice as wide)
+d96_4k    4, 32, 4096, 96        yes     forward + backward, bf16, head dimension 96
 ========  =====================  ======  ========================================================
 
 Decoding workloads (queries [B, H, Nq, d] against a key/value cache [B, H, Nk, d]; the queries are the
@@ -30,7 +31,7 @@ specdec_32k  4, 32, 8, 32768, 128        yes     8 draft tokens verified at once
 ===========  ==========================  ======  ===================================================
 
 Seeds: tensor t of workload c uses ``torch.Generator().manual_seed(1000*c + t)`` with c the workload
-number 1..8 and t = 0 (Q), 1 (K), 2 (V), 3 (dO), 4 (positions of the enlarged keys).  Values are drawn
+number 1..9 and t = 0 (Q), 1 (K), 2 (V), 3 (dO), 4 (positions of the enlarged keys).  Values are drawn
 as float32 N(0, 1) on the CPU and rounded to the storage type, so every consumer sees identical inputs.
 """
 
@@ -83,6 +84,7 @@ WORKLOADS = {
         Workload(4, "long_16k", 1, 32, 16384, 128, causal=True, backward=True, large_keys=True),
         Workload(5, "fp8_8k", 4, 32, 8192, 128, causal=True, backward=False, fp8=True),
         Workload(8, "d256_4k", 4, 16, 4096, 256, causal=True, backward=True),
+        Workload(9, "d96_4k", 4, 32, 4096, 96, causal=True, backward=True),
     ]
 }
 
