@@ -283,6 +283,66 @@ def fp8_forward(fa, workloads, lib, steps, warmup):
             "flops": w.fwd_flops()}
 
 
+def fp8_backward(fa, workloads, lib, steps, warmup):
+    """Secondary measurement: the FP8 backward (fa_bwd_fp8: widening of the e4m3 codes, D, dK/dV,
+    dQ) on fp8bwd_8k with O and LSE from the FP8 forward, timed with events; FLOPs 2.5× the forward
+    by the usual convention.  The FP8 forward is timed as well, for the whole fp8 step."""
+    import torch
+    w = workloads.WORKLOADS["fp8bwd_8k"]
+    B, H, N, d = w.shape()
+    log(f"[bench] secondary: {w.name} fp8 backward B={B} H={H} N={N} d={d} causal={w.causal}")
+    inp = workloads.make_inputs(w.name)
+    dev = torch.device("cuda:0")
+    q8, k8, v8, do = (inp[x].to(dev) for x in ("q8", "k8", "v8", "do"))
+    o = torch.empty((B, H, N, d), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    dq, dk, dv = (torch.empty_like(o) for _ in range(3))
+    ws_bytes = fa.bwd_fp8_workspace_bytes(B, H, N, d)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    sp = stream.cuda_stream
+    c = int(w.causal)
+
+    def fwd():
+        code = lib.fa_fwd_fp8(q8.data_ptr(), k8.data_ptr(), v8.data_ptr(), inp["sq"], inp["sk"],
+                              inp["sv"], o.data_ptr(), lse.data_ptr(), B, H, N, d, c, w.scale, sp)
+        if code != 0:
+            raise fa.FaError("fa_fwd_fp8", code, fa.status_str(code))
+
+    def bwd():
+        code = lib.fa_bwd_fp8(q8.data_ptr(), k8.data_ptr(), v8.data_ptr(), inp["sq"], inp["sk"],
+                              inp["sv"], o.data_ptr(), lse.data_ptr(), do.data_ptr(), dq.data_ptr(),
+                              dk.data_ptr(), dv.data_ptr(), ws.data_ptr(), ws_bytes, B, H, N, d, c,
+                              w.scale, sp)
+        if code != 0:
+            raise fa.FaError("fa_bwd_fp8", code, fa.status_str(code))
+
+    for _ in range(warmup):
+        fwd()
+        bwd()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    for e in ev:
+        e[0].record(stream)
+        fwd()
+        e[1].record(stream)
+        bwd()
+        e[2].record(stream)
+    torch.cuda.synchronize(dev)
+    fwd_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / steps
+    bwd_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / steps
+    fwd_f, bwd_f = w.fwd_flops(), w.bwd_flops()
+    out = {"workload": w.name, "kernels": ["e4m3_to_bf16_kernel", "bwd_pre_kernel",
+                                           "bwd_dkdv_kernel", "bwd_dq_kernel"],
+           "bwd_ms": bwd_ms, "bwd_tflops": bwd_f / (bwd_ms * 1e-3) / 1e12, "fwd_ms": fwd_ms,
+           "step_tflops": (fwd_f + bwd_f) / ((fwd_ms + bwd_ms) * 1e-3) / 1e12,
+           "bound": "mfma", "peak": BF16_PEAK_TFLOPS, "flops": bwd_f,
+           "workspace_bytes": ws_bytes}
+    out["frac"] = out["bwd_tflops"] / BF16_PEAK_TFLOPS
+    del q8, k8, v8, do, o, lse, dq, dk, dv, ws
+    torch.cuda.empty_cache()
+    return out
+
+
 def fwd_bwd_secondary(fa, workloads, lib, name, steps, warmup):
     """Secondary measurement: forward + backward of another bf16 workload (d256_4k, d96_4k: head
     dimensions 256 and 96), each phase bracketed by events; TFLOP/s by the same FLOP convention as
@@ -356,7 +416,7 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle work for the cpu_baseline leg (0 skips it)")
     ap.add_argument("--no-fp8", action="store_true",
-                    help="skip the secondary FP8 forward measurement (fp8_8k workload)")
+                    help="skip the secondary FP8 measurements (fp8_8k forward, fp8bwd_8k backward)")
     ap.add_argument("--no-head-dims", action="store_true",
                     help="skip the secondary measurements at head dimensions 256 and 96 "
                          "(d256_4k, d96_4k workloads)")
@@ -506,6 +566,7 @@ def main():
     secondary = {}
     if not args.no_fp8:
         secondary["fp8_8k_fwd"] = fp8_forward(fa, workloads, lib, args.steps, args.warmup)
+        secondary["fp8bwd_8k_bwd"] = fp8_backward(fa, workloads, lib, args.steps, args.warmup)
     if not args.no_head_dims:
         for name in ("d256_4k", "d96_4k"):
             secondary[name + "_fwd_bwd"] = fwd_bwd_secondary(fa, workloads, lib, name, args.steps,

@@ -115,6 +115,28 @@ fa_status fa_bwd_dq(const void* q, const void* k, const void* v, const float* ls
                     int B, int H, int N, int d, int causal, float softmax_scale,
                     hipStream_t stream);
 
+/*
+ * Backward pass of the FP8 forward (fa_fwd_fp8): the gradients of O = softmax(scale · Q Kᵀ) V with
+ * respect to the dequantised inputs Q = q8 · q_descale, K = k8 · k_descale, V = v8 · v_descale
+ * ("Anatomy ...", sections "How does FlashAttention save memory in the backward pass?" and "What
+ * changed between FlashAttention 1, 2, and 3?").  The e4m3 codes are widened exactly to bf16 images
+ * in the workspace and the bf16 backward runs on them with the descales folded into its scalar
+ * factors; the products run on bf16 matrix cores with fp32 accumulation.
+ *   q8, k8, v8   [B,H,N,d] e4m3fn codes as given to fa_fwd_fp8; descales finite and > 0.
+ *   o, lse       fa_fwd_fp8's outputs for those inputs;  dout [B,H,N,d] bf16 upstream gradient.
+ *   dq, dk, dv   [B,H,N,d] bf16 outputs.
+ *   workspace    at least fa_bwd_fp8_workspace_bytes(B,H,N,d) bytes, 256-byte aligned, owned by the
+ *                caller (D, then the bf16 images of q8, k8, v8); contents on entry do not matter.
+ * d as for fa_bwd.  Errors as for fa_bwd; FA_ERR_UNSUPPORTED also when a descale, or a product of the
+ * softmax scale with two descales, is not a positive normal fp32 number.
+ */
+size_t fa_bwd_fp8_workspace_bytes(int B, int H, int N, int d);
+fa_status fa_bwd_fp8(const void* q8, const void* k8, const void* v8, float q_descale,
+                     float k_descale, float v_descale, const void* o, const float* lse,
+                     const void* dout, void* dq, void* dk, void* dv, void* workspace,
+                     size_t workspace_bytes, int B, int H, int N, int d, int causal,
+                     float softmax_scale, hipStream_t stream);
+
 /* ---------------------------------------------------------------------------------------------------
  * Decoding against a key/value cache: a few new queries per (batch, head) attend over Nk cached keys,
  * the inference use the pages pair FlashAttention with ("flash attention" glossary entry, paragraph on

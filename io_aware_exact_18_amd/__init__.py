@@ -75,6 +75,10 @@ def library():
         lib.fa_decode_workspace_bytes.restype = sz
         lib.fa_decode.argtypes = [vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, i, f, vp]
         lib.fa_decode.restype = i
+        lib.fa_bwd_fp8_workspace_bytes.argtypes = [i, i, i, i]
+        lib.fa_bwd_fp8_workspace_bytes.restype = sz
+        lib.fa_bwd_fp8.argtypes = ([vp, vp, vp, f, f, f] + [vp] * 7 + [sz, i, i, i, i, i, f, vp])
+        lib.fa_bwd_fp8.restype = i
         _lib = lib
     return _lib
 
@@ -214,6 +218,41 @@ def bwd(q, k, v, o, lse, dout, causal, scale=None, workspace=None):
                                 dv.data_ptr(), workspace.data_ptr(), workspace.numel(), B, H, N, d,
                                 int(bool(causal)), _scale(scale, d), _stream(q.device))
     _check("fa_bwd", code)
+    return dq, dk, dv
+
+
+def bwd_fp8_workspace_bytes(B, H, N, d):
+    return int(library().fa_bwd_fp8_workspace_bytes(B, H, N, d))
+
+
+def bwd_fp8(q8, k8, v8, q_descale, k_descale, v_descale, o, lse, dout, causal, scale=None,
+            workspace=None):
+    """Backward of the FP8 forward: e4m3fn codes with their descales, fwd_fp8's (o, lse) and a bf16
+    upstream gradient in; (dq, dk, dv) bf16 out, the gradients with respect to the dequantised
+    inputs.  ``workspace``: optional uint8 device tensor of ``bwd_fp8_workspace_bytes`` bytes."""
+    _require(q8, "q8", torch.float8_e4m3fn)
+    if q8.dim() != 4:
+        raise ValueError("q8 must be [B, H, N, d]")
+    _require(k8, "k8", torch.float8_e4m3fn, q8.shape)
+    _require(v8, "v8", torch.float8_e4m3fn, q8.shape)
+    _require(o, "o", torch.bfloat16, q8.shape)
+    _require(dout, "dout", torch.bfloat16, q8.shape)
+    B, H, N, d = q8.shape
+    _require(lse, "lse", torch.float32, (B, H, N))
+    need = bwd_fp8_workspace_bytes(B, H, N, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q8.device)
+    else:
+        _require(workspace, "workspace", torch.uint8)
+    dq, dk, dv = (torch.empty((B, H, N, d), dtype=torch.bfloat16, device=q8.device)
+                  for _ in range(3))
+    with torch.cuda.device(q8.device):
+        code = library().fa_bwd_fp8(q8.data_ptr(), k8.data_ptr(), v8.data_ptr(), float(q_descale),
+                                    float(k_descale), float(v_descale), o.data_ptr(),
+                                    lse.data_ptr(), dout.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                                    dv.data_ptr(), workspace.data_ptr(), workspace.numel(), B, H,
+                                    N, d, int(bool(causal)), _scale(scale, d), _stream(q8.device))
+    _check("fa_bwd_fp8", code)
     return dq, dk, dv
 
 

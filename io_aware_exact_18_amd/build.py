@@ -18,7 +18,8 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(PKG_DIR, "libfa.so")
 ARCH = "gfx950"
 
-SOURCES = ["fa_api.hip", "fa_fwd.hip", "fa_bwd.hip", "fa_fwd_fp8.hip", "fa_decode.hip"]
+SOURCES = ["fa_api.hip", "fa_fwd.hip", "fa_bwd.hip", "fa_fwd_fp8.hip", "fa_decode.hip",
+           "fa_bwd_fp8.hip"]
 
 COMMON_FLAGS = [
     f"--offload-arch={ARCH}",

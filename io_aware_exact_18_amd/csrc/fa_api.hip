@@ -146,7 +146,7 @@ fa_status fa_bwd_dkdv(const void* q, const void* k, const void* v, const float* 
   a.dk = dk;
   a.dv = dv;
   a.causal = causal ? 1 : 0;
-  a.scale = softmax_scale;
+  a.scale = a.dk_scale = a.dq_scale = softmax_scale;
   return fa::launch_bwd_dkdv(a, stream) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
@@ -167,7 +167,7 @@ fa_status fa_bwd_dq(const void* q, const void* k, const void* v, const float* ls
   a.dout = dout;
   a.dq = dq;
   a.causal = causal ? 1 : 0;
-  a.scale = softmax_scale;
+  a.scale = a.dk_scale = a.dq_scale = softmax_scale;
   return fa::launch_bwd_dq(a, stream) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
@@ -216,7 +216,64 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
   a.dk = dk;
   a.dv = dv;
   a.causal = causal ? 1 : 0;
-  a.scale = softmax_scale;
+  a.scale = a.dk_scale = a.dq_scale = softmax_scale;
+  if (fa::launch_bwd_pre(a, stream) != hipSuccess) return FA_ERR_LAUNCH;
+  if (fa::launch_bwd_dkdv(a, stream) != hipSuccess) return FA_ERR_LAUNCH;
+  if (fa::launch_bwd_dq(a, stream) != hipSuccess) return FA_ERR_LAUNCH;
+  return FA_OK;
+}
+
+size_t fa_bwd_fp8_workspace_bytes(int B, int H, int N, int d) {
+  if (check_shape(B, H, N, d, 2) != FA_OK) return 0;
+  return fa::bwd_fp8_workspace_bytes(B, H, N, d);
+}
+
+fa_status fa_bwd_fp8(const void* q8, const void* k8, const void* v8, float q_descale,
+                     float k_descale, float v_descale, const void* o, const float* lse,
+                     const void* dout, void* dq, void* dk, void* dv, void* workspace,
+                     size_t workspace_bytes, int B, int H, int N, int d, int causal,
+                     float softmax_scale, hipStream_t stream) {
+  if (!q8 || !k8 || !v8 || !o || !lse || !dout || !dq || !dk || !dv) return FA_ERR_NULL;
+  fa::BwdArgs a{};
+  const void* ptrs[] = {q8, k8, v8, o, lse, dout, dq, dk, dv};
+  fa_status st = check_bwd(ptrs, 9, workspace, workspace_bytes, B, H, N, d, &a);
+  if (st != FA_OK) return st;
+  if (!good_scale(softmax_scale) || !good_scale(q_descale) || !good_scale(k_descale) ||
+      !good_scale(v_descale))
+    return FA_ERR_UNSUPPORTED;
+  if (workspace_bytes < fa::bwd_fp8_workspace_bytes(B, H, N, d)) return FA_ERR_WORKSPACE;
+  // The scales must stay normal fp32 numbers once folded.
+  const float score_scale = softmax_scale * q_descale * k_descale;
+  const float dk_scale = softmax_scale * v_descale * q_descale;
+  const float dq_scale = softmax_scale * v_descale * k_descale;
+  const float delta_mult = 1.f / v_descale;
+  if (!good_scale(score_scale) || !good_scale(dk_scale) || !good_scale(dq_scale) ||
+      !good_scale(delta_mult) || !isnormal(score_scale) || !isnormal(dk_scale) ||
+      !isnormal(dq_scale) || !isnormal(delta_mult))
+    return FA_ERR_UNSUPPORTED;
+  const size_t n = (size_t)B * H * N * d;
+  char* ws = (char*)workspace;
+  char* qc = ws + fa::bwd_delta_bytes(B, H, N);
+  char* kc = qc + fa::bwd_fp8_image_bytes(B, H, N, d);
+  char* vc = kc + fa::bwd_fp8_image_bytes(B, H, N, d);
+  a.q = qc;
+  a.k = kc;
+  a.v = vc;
+  a.o = o;
+  a.lse = lse;
+  a.dout = dout;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.causal = causal ? 1 : 0;
+  a.scale = score_scale;
+  a.dk_scale = dk_scale;
+  a.dq_scale = dq_scale;
+  a.delta_mult = delta_mult;
+  if (fa::launch_e4m3_to_bf16(q8, qc, n, stream) != hipSuccess ||
+      fa::launch_e4m3_to_bf16(k8, kc, n, stream) != hipSuccess ||
+      fa::launch_e4m3_to_bf16(v8, vc, n, stream) != hipSuccess)
+    return FA_ERR_LAUNCH;
   if (fa::launch_bwd_pre(a, stream) != hipSuccess) return FA_ERR_LAUNCH;
   if (fa::launch_bwd_dkdv(a, stream) != hipSuccess) return FA_ERR_LAUNCH;
   if (fa::launch_bwd_dq(a, stream) != hipSuccess) return FA_ERR_LAUNCH;

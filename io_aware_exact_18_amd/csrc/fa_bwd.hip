@@ -46,7 +46,8 @@ constexpr int pre_tpr() { return D == 96 ? 4 : D / 8; }
 template <int D>
 __global__ __launch_bounds__(kThreads) void bwd_pre_kernel(const bf16* __restrict__ O,
                                                            const bf16* __restrict__ dO,
-                                                           float* __restrict__ delta, long rows) {
+                                                           float* __restrict__ delta, long rows,
+                                                           float mult) {
   constexpr int TPR = pre_tpr<D>();  // threads per row
   constexpr int RUNS = D / (8 * TPR);
   static_assert(RUNS * 8 * TPR == D && (TPR & (TPR - 1)) == 0, "row split");
@@ -67,7 +68,7 @@ __global__ __launch_bounds__(kThreads) void bwd_pre_kernel(const bf16* __restric
   }
 #pragma unroll
   for (int off = TPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, TPR);
-  if (row < rows && part == 0) delta[row] = acc;
+  if (row < rows && part == 0) delta[row] = acc * mult;
 }
 
 // ---------------------------------------------------------------------------------------------------
@@ -416,7 +417,8 @@ hipError_t launch_pre(const BwdArgs& a, hipStream_t stream) {
   constexpr int rows_per_block = kThreads / pre_tpr<D>();
   hipLaunchKernelGGL((bwd_pre_kernel<D>),
                      dim3((unsigned)((rows + rows_per_block - 1) / rows_per_block)),
-                     dim3(kThreads), 0, stream, (const bf16*)a.o, (const bf16*)a.dout, a.delta, rows);
+                     dim3(kThreads), 0, stream, (const bf16*)a.o, (const bf16*)a.dout, a.delta, rows,
+                     a.delta_mult);
   return hipGetLastError();
 }
 
@@ -428,7 +430,7 @@ hipError_t launch_dkdv_pass(const BwdArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, OUT>), dim3(total), dim3(kThreads), 0, stream,
                      (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, a.lse,
                      (const bf16*)a.dout, (const float*)a.delta, (bf16*)a.dk, (bf16*)a.dv, a.N, nkt,
-                     a.scale, a.scale * kLog2e, remap);
+                     a.dk_scale, a.scale * kLog2e, remap);
   return hipGetLastError();
 }
 
@@ -450,7 +452,7 @@ hipError_t launch_dq(const BwdArgs& a, hipStream_t stream) {
   const int remap = (total % 8u == 0u) ? 1 : 0;
   hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3(total), dim3(kThreads), 0, stream,
                      (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, a.lse,
-                     (const bf16*)a.dout, (const float*)a.delta, (bf16*)a.dq, a.N, nqt, a.scale,
+                     (const bf16*)a.dout, (const float*)a.delta, (bf16*)a.dq, a.N, nqt, a.dq_scale,
                      a.scale * kLog2e, remap);
   return hipGetLastError();
 }

@@ -37,9 +37,12 @@ struct BwdArgs {
   void* dq;
   void* dk;
   void* dv;
-  float* delta;  // fp32 [B,H,N] workspace: D_i = dO_i · O_i
+  float* delta;  // fp32 [B,H,N] workspace: D_i = (dO_i · O_i) · delta_mult
   int B, H, N, d, causal;
-  float scale;
+  float scale;             // multiplier of the products of q and k as stored (the softmax scale)
+  float dk_scale = 0.f;    // dK = dk_scale · Σ_i dS_ij q_i and dQ = dq_scale · Σ_j dS_ij k_j, with
+  float dq_scale = 0.f;    // dS computed from v as stored and D; both equal `scale` for bf16 inputs
+  float delta_mult = 1.f;  // 1 for bf16 inputs; 1 / v_descale when v holds e4m3 codes
 };
 
 struct DecodeArgs {
@@ -87,11 +90,21 @@ hipError_t launch_bwd_pre(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+// n e4m3fn codes (n a multiple of 16, both pointers 16-byte aligned) → n bf16 values equal to the
+// codes' values (exact: every e4m3 value is a bf16 value).
+hipError_t launch_e4m3_to_bf16(const void* src, void* dst, size_t n, hipStream_t stream);
 
 // Backward workspace: the fp32 [B,H,N] array D, rounded up to 256 bytes.
 inline size_t round_up_256(size_t x) { return (x + 255u) & ~(size_t)255u; }
 inline size_t bwd_delta_bytes(int B, int H, int N) {
   return round_up_256((size_t)B * H * N * sizeof(float));
+}
+// FP8 backward workspace: D, then bf16 images of the q, k, v codes, each rounded up to 256 bytes.
+inline size_t bwd_fp8_image_bytes(int B, int H, int N, int d) {
+  return round_up_256((size_t)B * H * N * d * 2u);
+}
+inline size_t bwd_fp8_workspace_bytes(int B, int H, int N, int d) {
+  return bwd_delta_bytes(B, H, N) + 3 * bwd_fp8_image_bytes(B, H, N, d);
 }
 
 }  // namespace fa

@@ -36,6 +36,9 @@ def lib():
     lib.fa_decode_workspace_bytes.argtypes = [i, i, i, i, i]
     lib.fa_decode_workspace_bytes.restype = sz
     lib.fa_decode.argtypes = [vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, i, f, vp]
+    lib.fa_bwd_fp8_workspace_bytes.argtypes = [i, i, i, i]
+    lib.fa_bwd_fp8_workspace_bytes.restype = sz
+    lib.fa_bwd_fp8.argtypes = [vp, vp, vp, f, f, f] + [vp] * 7 + [sz, i, i, i, i, i, f, vp]
     return lib
 
 
@@ -44,7 +47,8 @@ def test_exports_match_header(lib):
     declared = set(re.findall(r"^\s*(?:fa_status|size_t|const char\*)\s+(fa_\w+)\s*\(", text, re.M))
     assert declared == {"fa_fwd", "fa_fwd_fp8", "fa_bwd_workspace_bytes", "fa_bwd", "fa_status_str",
                         "fa_bwd_preprocess", "fa_bwd_dkdv", "fa_bwd_dq", "fa_device_info",
-                        "fa_decode", "fa_decode_workspace_bytes"}
+                        "fa_decode", "fa_decode_workspace_bytes", "fa_bwd_fp8",
+                        "fa_bwd_fp8_workspace_bytes"}
     for name in declared:
         assert hasattr(lib, name), name
 
@@ -140,6 +144,41 @@ def test_bwd_phase_rejections(lib):
     assert lib.fa_bwd_dq(P, P, P, P, P, P, P + 128, ws, 1, 1, 64, 64, 1, 0.1, None) == ALIGN
     assert lib.fa_bwd_dq(P, P, P, P, P, P, P, ws, 1, 0, 64, 64, 1, 0.1, None) == SHAPE
     assert lib.fa_bwd_dq(P, P, P, P, MIS, P, P, ws, 1, 1, 64, 64, 1, 0.1, None) == ALIGN
+
+
+def test_bwd_fp8_workspace_formula(lib):
+    def up(x):
+        return (x + 255) // 256 * 256
+    for B, H, N, d in ((1, 1, 1, 64), (4, 32, 8192, 128), (1, 3, 17, 96), (2, 2, 300, 256)):
+        want = up(B * H * N * 4) + 3 * up(B * H * N * d * 2)
+        assert lib.fa_bwd_fp8_workspace_bytes(B, H, N, d) == want
+    assert lib.fa_bwd_fp8_workspace_bytes(1, 1, 64, 80) == 0
+    assert lib.fa_bwd_fp8_workspace_bytes(0, 1, 64, 128) == 0
+
+
+def bwd8(lib, q8=P, dq=P, o=P, ws=P, ws_bytes=1 << 30, N=64, d=128, qs=1.0, ks=1.0, vs=1.0,
+         scale=0.09):
+    return lib.fa_bwd_fp8(q8, P, P, qs, ks, vs, o, P, P, dq, P, P, ws, ws_bytes, 1, 1, N, d, 1,
+                          scale, None)
+
+
+def test_bwd_fp8_rejections(lib):
+    assert bwd8(lib, q8=None) == NULL
+    assert bwd8(lib, o=None) == NULL
+    assert bwd8(lib, N=0) == SHAPE
+    assert bwd8(lib, d=80) == UNSUP
+    for bad in (0.0, -1.0, math.inf, math.nan):
+        assert bwd8(lib, qs=bad) == UNSUP
+        assert bwd8(lib, vs=bad) == UNSUP
+        assert bwd8(lib, scale=bad) == UNSUP
+    assert bwd8(lib, qs=1e-30, ks=1e-30) == UNSUP    # folded score scale underflows fp32 normals
+    assert bwd8(lib, vs=3e38, qs=10.0) == UNSUP      # folded dK scale overflows fp32
+    need = lib.fa_bwd_fp8_workspace_bytes(1, 1, 64, 128)
+    assert bwd8(lib, ws_bytes=need - 1) == WORKSPACE
+    assert bwd8(lib, ws=None) == WORKSPACE
+    assert bwd8(lib, ws=P + 16) == ALIGN
+    assert bwd8(lib, q8=MIS) == ALIGN
+    assert bwd8(lib, dq=MIS) == ALIGN
 
 
 def test_binding_fails_loudly_without_tensors_on_gpu():
