@@ -417,6 +417,9 @@ def main():
                     help="seconds of oracle work for the cpu_baseline leg (0 skips it)")
     ap.add_argument("--no-fp8", action="store_true",
                     help="skip the secondary FP8 measurements (fp8_8k forward, fp8bwd_8k backward)")
+    ap.add_argument("--no-fp8-bwd", action="store_true",
+                    help="skip only the secondary FP8 backward measurement (fp8bwd_8k), whose "
+                         "kernels are the causal d=128 backward instantiations")
     ap.add_argument("--no-head-dims", action="store_true",
                     help="skip the secondary measurements at head dimensions 256 and 96 "
                          "(d256_4k, d96_4k workloads)")
@@ -566,7 +569,8 @@ def main():
     secondary = {}
     if not args.no_fp8:
         secondary["fp8_8k_fwd"] = fp8_forward(fa, workloads, lib, args.steps, args.warmup)
-        secondary["fp8bwd_8k_bwd"] = fp8_backward(fa, workloads, lib, args.steps, args.warmup)
+        if not args.no_fp8_bwd:
+            secondary["fp8bwd_8k_bwd"] = fp8_backward(fa, workloads, lib, args.steps, args.warmup)
     if not args.no_head_dims:
         for name in ("d256_4k", "d96_4k"):
             secondary[name + "_fwd_bwd"] = fwd_bwd_secondary(fa, workloads, lib, name, args.steps,
