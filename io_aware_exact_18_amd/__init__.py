@@ -11,6 +11,9 @@ Entry points (same names as the C ABI, without the ``fa_`` prefix):
   bwd(q, k, v, o, lse, dout, causal, scale=None, workspace=None) -> (dq, dk, dv)
   bwd_workspace_bytes(B, H, N, d) -> int
   bwd_preprocess / bwd_dkdv / bwd_dq — the three phases fa_bwd runs, for timing them apart
+  bwd_fp8(q8, k8, v8, q_descale, k_descale, v_descale, o, lse, dout, causal, scale=None,
+          workspace=None) -> (dq, dk, dv)      (the backward of fwd_fp8)
+  bwd_fp8_workspace_bytes(B, H, N, d) -> int
   status_str(code) -> str
   decode(q, k, v, causal, scale=None, workspace=None) -> (o, lse)   (q: [B,H,Nq,d], k/v: [B,H,Nk,d])
   decode_workspace_bytes(B, H, Nq, Nk, d) -> int
@@ -24,8 +27,8 @@ import os
 import torch
 
 __all__ = ["fwd", "fwd_fp8", "bwd", "bwd_workspace_bytes", "bwd_preprocess", "bwd_dkdv",
-           "bwd_dq", "decode", "decode_workspace_bytes", "status_str", "device_info", "FaError",
-           "library", "LIB_PATH"]
+           "bwd_dq", "bwd_fp8", "bwd_fp8_workspace_bytes", "decode", "decode_workspace_bytes",
+           "status_str", "device_info", "FaError", "library", "LIB_PATH"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
 
@@ -99,11 +102,15 @@ def _check(fn, code):
         raise FaError(fn, code, status_str(code))
 
 
-def _require(t, name, dtype, shape=None):
+def _require(t, name, dtype, shape=None, device=None):
+    """Checks one tensor argument: a contiguous ROCm tensor of this dtype (and shape, and the same
+    device as the call's first tensor when ``device`` is given)."""
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
     if t.device.type != "cuda":
         raise ValueError(f"{name} must be on a ROCm device, got {t.device}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, the call's tensors are on {device}")
     if t.dtype != dtype:
         raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
     if not t.is_contiguous():
@@ -125,8 +132,8 @@ def fwd(q, k, v, causal, scale=None):
     _require(q, "q", torch.bfloat16)
     if q.dim() != 4:
         raise ValueError("q must be [B, H, N, d]")
-    _require(k, "k", torch.bfloat16, q.shape)
-    _require(v, "v", torch.bfloat16, q.shape)
+    _require(k, "k", torch.bfloat16, q.shape, device=q.device)
+    _require(v, "v", torch.bfloat16, q.shape, device=q.device)
     B, H, N, d = q.shape
     o = torch.empty_like(q)
     lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
@@ -150,16 +157,18 @@ def decode(q, k, v, causal, scale=None, workspace=None):
     if q.dim() != 4:
         raise ValueError("q must be [B, H, Nq, d]")
     B, H, Nq, d = q.shape
-    _require(k, "k", torch.bfloat16)
+    _require(k, "k", torch.bfloat16, device=q.device)
     if k.dim() != 4 or k.shape[0] != B or k.shape[1] != H or k.shape[3] != d:
         raise ValueError(f"k has shape {tuple(k.shape)}, expected [{B}, {H}, Nk, {d}]")
     Nk = k.shape[2]
-    _require(v, "v", torch.bfloat16, k.shape)
+    _require(v, "v", torch.bfloat16, k.shape, device=q.device)
     o = torch.empty_like(q)
     lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
     ws_bytes = decode_workspace_bytes(B, H, Nq, Nk, d)
     if workspace is None:
         workspace = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=q.device)
+    else:
+        _require(workspace, "workspace", torch.uint8, device=q.device)
     with torch.cuda.device(q.device):
         code = library().fa_decode(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
                                    lse.data_ptr(), workspace.data_ptr(), workspace.numel(), B, H,
@@ -173,8 +182,8 @@ def fwd_fp8(q8, k8, v8, q_descale, k_descale, v_descale, causal, scale=None):
     _require(q8, "q8", torch.float8_e4m3fn)
     if q8.dim() != 4:
         raise ValueError("q8 must be [B, H, N, d]")
-    _require(k8, "k8", torch.float8_e4m3fn, q8.shape)
-    _require(v8, "v8", torch.float8_e4m3fn, q8.shape)
+    _require(k8, "k8", torch.float8_e4m3fn, q8.shape, device=q8.device)
+    _require(v8, "v8", torch.float8_e4m3fn, q8.shape, device=q8.device)
     B, H, N, d = q8.shape
     o = torch.empty((B, H, N, d), dtype=torch.bfloat16, device=q8.device)
     lse = torch.empty((B, H, N), dtype=torch.float32, device=q8.device)
@@ -201,14 +210,14 @@ def bwd(q, k, v, o, lse, dout, causal, scale=None, workspace=None):
     if q.dim() != 4:
         raise ValueError("q must be [B, H, N, d]")
     for t, name in ((k, "k"), (v, "v"), (o, "o"), (dout, "dout")):
-        _require(t, name, torch.bfloat16, q.shape)
+        _require(t, name, torch.bfloat16, q.shape, device=q.device)
     B, H, N, d = q.shape
-    _require(lse, "lse", torch.float32, (B, H, N))
+    _require(lse, "lse", torch.float32, (B, H, N), device=q.device)
     need = bwd_workspace_bytes(B, H, N, d)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     else:
-        _require(workspace, "workspace", torch.uint8)
+        _require(workspace, "workspace", torch.uint8, device=q.device)
     dq = torch.empty_like(q)
     dk = torch.empty_like(q)
     dv = torch.empty_like(q)
@@ -233,17 +242,17 @@ def bwd_fp8(q8, k8, v8, q_descale, k_descale, v_descale, o, lse, dout, causal, s
     _require(q8, "q8", torch.float8_e4m3fn)
     if q8.dim() != 4:
         raise ValueError("q8 must be [B, H, N, d]")
-    _require(k8, "k8", torch.float8_e4m3fn, q8.shape)
-    _require(v8, "v8", torch.float8_e4m3fn, q8.shape)
-    _require(o, "o", torch.bfloat16, q8.shape)
-    _require(dout, "dout", torch.bfloat16, q8.shape)
+    _require(k8, "k8", torch.float8_e4m3fn, q8.shape, device=q8.device)
+    _require(v8, "v8", torch.float8_e4m3fn, q8.shape, device=q8.device)
+    _require(o, "o", torch.bfloat16, q8.shape, device=q8.device)
+    _require(dout, "dout", torch.bfloat16, q8.shape, device=q8.device)
     B, H, N, d = q8.shape
-    _require(lse, "lse", torch.float32, (B, H, N))
+    _require(lse, "lse", torch.float32, (B, H, N), device=q8.device)
     need = bwd_fp8_workspace_bytes(B, H, N, d)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q8.device)
     else:
-        _require(workspace, "workspace", torch.uint8)
+        _require(workspace, "workspace", torch.uint8, device=q8.device)
     dq, dk, dv = (torch.empty((B, H, N, d), dtype=torch.bfloat16, device=q8.device)
                   for _ in range(3))
     with torch.cuda.device(q8.device):
@@ -259,8 +268,8 @@ def bwd_fp8(q8, k8, v8, q_descale, k_descale, v_descale, o, lse, dout, causal, s
 def bwd_preprocess(o, dout, workspace):
     """Phase 1 of the backward: D = rowsum(dO ∘ O) into ``workspace``."""
     _require(o, "o", torch.bfloat16)
-    _require(dout, "dout", torch.bfloat16, o.shape)
-    _require(workspace, "workspace", torch.uint8)
+    _require(dout, "dout", torch.bfloat16, o.shape, device=o.device)
+    _require(workspace, "workspace", torch.uint8, device=o.device)
     B, H, N, d = o.shape
     with torch.cuda.device(o.device):
         code = library().fa_bwd_preprocess(o.data_ptr(), dout.data_ptr(), workspace.data_ptr(),
@@ -271,10 +280,10 @@ def bwd_preprocess(o, dout, workspace):
 def _bwd_inputs(q, k, v, lse, dout, workspace, outs):
     _require(q, "q", torch.bfloat16)
     for t, name in ((k, "k"), (v, "v"), (dout, "dout"), *outs):
-        _require(t, name, torch.bfloat16, q.shape)
+        _require(t, name, torch.bfloat16, q.shape, device=q.device)
     B, H, N, d = q.shape
-    _require(lse, "lse", torch.float32, (B, H, N))
-    _require(workspace, "workspace", torch.uint8)
+    _require(lse, "lse", torch.float32, (B, H, N), device=q.device)
+    _require(workspace, "workspace", torch.uint8, device=q.device)
     return B, H, N, d
 
 

@@ -236,3 +236,15 @@ def test_decode_rejections(lib):
     assert decode(lib, ws_bytes=need - 1) == WORKSPACE
     assert decode(lib, k=MIS) == ALIGN
     assert decode(lib, ws=P + 16) == ALIGN
+
+
+def test_binding_rejects_mixed_devices_without_a_gpu():
+    """Argument checks run before any device work: a CPU tensor among device tensors is refused
+    (checked here with the first tensor on the CPU, the only device this machine has)."""
+    import torch
+    import io_aware_exact_18_amd as fa
+    x = torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16)
+    for call in (lambda: fa.decode(x, x, x, True), lambda: fa.bwd(x, x, x, x, x[..., 0].float(), x,
+                                                                 True)):
+        with pytest.raises(ValueError):
+            call()
