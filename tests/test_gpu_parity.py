@@ -282,6 +282,19 @@ def test_wide_heads_many_tiles(d, causal):
     _check_bwd_heads(q, k, v, do, dq.cpu(), dk.cpu(), dv.cpu(), causal, scale, range(B * H))
 
 
+@pytest.mark.parametrize("scale", [0.03, 0.4])
+@pytest.mark.parametrize("d", [64, 96, 128])
+def test_fwd_bwd_other_softmax_scales(scale, d):
+    """A softmax scale other than 1/√d (flatter and sharper rows): the scale enters P in every kernel
+    and the dK, dQ epilogues, so a slip in its plumbing shows here."""
+    B, H, N = 1, 2, 300
+    g = torch.Generator().manual_seed(int(scale * 1000) + d)
+    q, k, v, do = (torch.randn(B, H, N, d, generator=g).to(torch.bfloat16) for _ in range(4))
+    o, lse, dq, dk, dv = _run_bwd(q, k, v, do, True, scale)
+    _check_fwd_heads(q, k, v, o.cpu(), lse.cpu(), True, scale, o_tol="bf16_store")
+    _check_bwd_heads(q, k, v, do, dq.cpu(), dk.cpu(), dv.cpu(), True, scale, range(B * H))
+
+
 @pytest.mark.parametrize("d", [96, 128, 256])
 def test_bwd_guarded(d):
     """Nothing is written past dQ, dK, dV or the workspace's documented size."""
