@@ -345,8 +345,8 @@ def fp8_backward(fa, workloads, lib, steps, warmup):
 
 def fwd_bwd_secondary(fa, workloads, lib, name, steps, warmup):
     """Secondary measurement: forward + backward of another bf16 workload (d256_4k, d96_4k: head
-    dimensions 256 and 96), each phase bracketed by events; TFLOP/s by the same FLOP convention as
-    the headline."""
+    dimensions 256 and 96; d64_2k, long_16k: the other forward + backward workloads), each phase
+    bracketed by events; TFLOP/s by the same FLOP convention as the headline."""
     import torch
     w = workloads.WORKLOADS[name]
     B, H, N, d = w.shape()
@@ -423,6 +423,9 @@ def main():
     ap.add_argument("--no-head-dims", action="store_true",
                     help="skip the secondary measurements at head dimensions 256 and 96 "
                          "(d256_4k, d96_4k workloads)")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the secondary measurements of the d64_2k and long_16k workloads "
+                         "(long_16k runs the causal d=128 kernel instantiations)")
     ap.add_argument("--no-decode", action="store_true",
                     help="skip the secondary decoding measurements (decode_32k, specdec_32k)")
     ap.add_argument("--traffic-sweep", action="store_true",
@@ -573,6 +576,10 @@ def main():
             secondary["fp8bwd_8k_bwd"] = fp8_backward(fa, workloads, lib, args.steps, args.warmup)
     if not args.no_head_dims:
         for name in ("d256_4k", "d96_4k"):
+            secondary[name + "_fwd_bwd"] = fwd_bwd_secondary(fa, workloads, lib, name, args.steps,
+                                                             args.warmup)
+    if not args.no_configs:
+        for name in ("d64_2k", "long_16k"):
             secondary[name + "_fwd_bwd"] = fwd_bwd_secondary(fa, workloads, lib, name, args.steps,
                                                              args.warmup)
     if not args.no_decode:
