@@ -215,6 +215,29 @@ def test_fwd_equal_scores_closed_form(d, causal):
     assert (lse.cpu().double() - lref).abs().max().item() <= 1e-5
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_fwd_output_rounding_is_rne(d):
+    """O is rounded to bf16 once, to nearest, ties to even.  With Q = 0 and two keys every
+    probability is exactly 1/2, and with V in ±[1, 2) the fp32 result (v0 + v1)/2 is exact and often
+    lies exactly halfway between two bf16 values, so O must equal its round-to-nearest-even image
+    bit for bit (ties included)."""
+    B, H, N = 1, 4, 2
+    g = torch.Generator().manual_seed(40 + d)
+    mag = 1.0 + torch.rand(B, H, N, d, generator=g)
+    sign = torch.where(torch.rand(B, H, N, d, generator=g) < 0.5, -1.0, 1.0)
+    v = (mag * sign).to(torch.bfloat16)
+    k = torch.randn(B, H, N, d, generator=g).to(torch.bfloat16)
+    q = torch.zeros(B, H, N, d, dtype=torch.bfloat16)
+    o, lse = _run_fwd(q, k, v, False, 1.0 / math.sqrt(d))
+    exact = (v[:, :, 0].float() + v[:, :, 1].float()) * 0.5  # exact in fp32
+    want = exact.to(torch.bfloat16)                           # torch rounds to nearest even
+    ties = int(((exact.view(torch.int32) & 0xFFFF) == 0x8000).sum())
+    assert ties > 0  # the case that tells RNE from other rounding modes occurs
+    for row in range(N):
+        assert torch.equal(o[:, :, row].cpu(), want), row
+    assert torch.allclose(lse.cpu(), torch.full((B, H, N), math.log(2.0)), atol=1e-6)
+
+
 @pytest.mark.parametrize("d", [64, 96, 128, 256])
 def test_fwd_causal_row0_exact(d):
     """Under the causal mask row 0 sees only key 0: O_0 = V_0 exactly, LSE_0 = scale·q_0·k_0."""
