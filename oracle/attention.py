@@ -49,6 +49,7 @@ __all__ = [
     "attention_fwd64",
     "attention_bwd64",
     "attention_rows64",
+    "attention_rows_dq64",
     "online_attention_head64",
     "brute_attention_head",
     "brute_attention_head_bwd",
@@ -180,6 +181,32 @@ def attention_rows64(q, k, v, rows, causal, scale):
         o[r] = (e / l) @ v[:end]
         lse[r] = m + np.log(l)
     return o, lse
+
+
+def attention_rows_dq64(q, k, v, do, rows, causal, scale):
+    """dQ for selected query rows of one head, each computed on its own.
+
+    Row i of dQ depends only on row i of P and of dP, so the chain rule of attention_head_bwd64
+    restricted to one row reads: over the allowed keys (all, or j ≤ i when causal),
+    p = softmax(scale · k_j·q_i), dp_j = dO_i·v_j, ds_j = p_j (dp_j − Σ_k p_k dp_k),
+    dq_i = scale · Σ_j ds_j k_j.  Cost O(N·d) per row, for sampled checks of long sequences.
+    Returns dq [len(rows), d].
+    """
+    q = _as64(q)
+    k = _as64(k)
+    v = _as64(v)
+    do = _as64(do)
+    rows = list(rows)
+    dq = np.empty((len(rows), k.shape[1]), dtype=np.float64)
+    for r, i in enumerate(rows):
+        end = i + 1 if causal else k.shape[0]
+        s = scale * (k[:end] @ q[i])
+        e = np.exp(s - np.max(s))
+        p = e / np.sum(e)
+        dp = v[:end] @ do[i]
+        ds = p * (dp - np.sum(p * dp))
+        dq[r] = scale * (ds @ k[:end])
+    return dq
 
 
 def online_attention_head64(q, k, v, causal, scale, tile_r, tile_c):

@@ -244,8 +244,8 @@ def pin_brute_force(orc):
 
 
 def pin_batched_and_rows(orc):
-    """The [B,H,N,d] drivers apply the per-head functions head by head, and the single-row function
-    agrees with the full forward."""
+    """The [B,H,N,d] drivers apply the per-head functions head by head, and the single-row functions
+    agree with the full forward and with the rows of the full backward's dQ."""
     r = _rng(22)
     q, k, v, do = (r.standard_normal((2, 3, 9, 4)) for _ in range(4))
     for causal in (False, True):
@@ -262,6 +262,9 @@ def pin_batched_and_rows(orc):
                 orow, lrow = orc.attention_rows64(q[b, h], k[b, h], v[b, h], rows, causal, 0.5)
                 assert np.max(np.abs(orow - oh[rows])) <= 1e-13
                 assert np.max(np.abs(lrow - lh[rows])) <= 1e-13
+                dqrow = orc.attention_rows_dq64(q[b, h], k[b, h], v[b, h], do[b, h], rows, causal,
+                                                0.5)
+                assert np.max(np.abs(dqrow - gh[0][rows])) <= 1e-13
 
 
 def pin_decode_rows_of_full(orc):

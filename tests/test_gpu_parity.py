@@ -411,6 +411,30 @@ def test_workload_long_full():
     _check_bwd_sums(inp["do"], dk, dv)
 
 
+def test_million_keys_one_head():
+    """One causal head of 2^20 keys, far past the workloads: blocks of query rows at the start, the
+    middle and the end against the oracle's row-restricted forms (attention_head_fwd64 with a query
+    offset for O and LSE, attention_rows_dq64 for dQ), and dK, dV through the exact sums."""
+    B, H, N, d = 1, 1, 1 << 20, 128
+    g = torch.Generator().manual_seed(1 << 20)
+    q, k, v, do = (torch.randn(B, H, N, d, generator=g).to(torch.bfloat16) for _ in range(4))
+    scale = 1.0 / math.sqrt(d)
+    o, lse, dq, dk, dv = _run_bwd(q, k, v, do, True, scale)
+    for t in (o, lse, dq, dk, dv):
+        assert bool(torch.isfinite(t).all())
+    q64, k64, v64, do64 = (x[0, 0].double().numpy() for x in (q, k, v, do))
+    o_c, l_c, dq_c = o[0, 0].cpu(), lse[0, 0].cpu(), dq[0, 0].cpu()
+    for r0 in (0, 77777, N // 2, N - 8):
+        rows = list(range(r0, r0 + 8))
+        o_ref, l_ref = oracle.attention_head_fwd64(q64[r0:r0 + 8], k64, v64, True, scale, q_offset=r0)
+        err = np.abs(_np64(o_c[r0:r0 + 8]) - o_ref)
+        assert np.all(err <= O_TOL + _half_ulp_bf16(o_ref)), (r0, float(err.max()))
+        assert np.abs(_np64(l_c[r0:r0 + 8]) - l_ref).max() <= 1e-3, r0
+        dq_ref = oracle.attention_rows_dq64(q64, k64, v64, do64, rows, True, scale)
+        assert _rel_fro(_np64(dq_c[r0:r0 + 8]), dq_ref) <= GRAD_TOL, r0
+    _check_bwd_sums(do, dk, dv)
+
+
 @pytest.mark.parametrize("d", [96, 128, 256])
 def test_bwd_phases_equal_fused_call(d):
     """fa_bwd_preprocess + fa_bwd_dkdv + fa_bwd_dq give bitwise what fa_bwd gives, and fa_bwd is

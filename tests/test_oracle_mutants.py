@@ -45,6 +45,8 @@ MUTANTS = [
      "s = np.where(j >= i + 1, -np.inf, s)\n            s = np.where(j == i, -np.inf, s)\n            m_new"),
     ("rows_causal_end", "end = i + 1 if causal else k.shape[0]", "end = i if causal else k.shape[0]"),
     ("rows_no_scale", "s = scale * (k[:end] @ q[i])", "s = (k[:end] @ q[i])"),
+    ("rows_dq_no_row_term", "ds = p * (dp - np.sum(p * dp))", "ds = p * dp"),
+    ("rows_dq_wrong_operand", "dp = v[:end] @ do[i]", "dp = k[:end] @ do[i]"),
     ("driver_wrong_head", "o[b, h], lse[b, h] = attention_head_fwd64(q[b, h], k[b, h], v[b, h], causal, scale)",
      "o[b, h], lse[b, h] = attention_head_fwd64(q[b, h], k[b, 0], v[b, h], causal, scale)"),
 ]
