@@ -77,7 +77,7 @@ __global__ __launch_bounds__(kThreads) void bwd_pre_kernel(const bf16* __restric
 // registers' worth of room it needs for the K fragments and the step's tiles; the dV pass needs
 // neither V nor dP, and the extra cost is one more S product per step.
 template <int D, bool CAUSAL, int OUT>
-__global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void bwd_dkdv_kernel(
+__global__ __launch_bounds__(kThreads, (D == 256 && OUT != 1) ? 1 : 2) void bwd_dkdv_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     const float* __restrict__ LSE, const bf16* __restrict__ dO, const float* __restrict__ Delta,
     bf16* __restrict__ dK, bf16* __restrict__ dV, int N, int nkt, float scale, float scale_log2,

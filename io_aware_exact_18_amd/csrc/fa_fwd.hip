@@ -28,6 +28,8 @@
 //     natural log on output.
 //   * Grid: one workgroup per (batch·head, query tile); query tiles of one head are kept on one XCD so
 //     the head's K/V stay in that XCD's L2; under the causal mask the heaviest tiles start first.
+//   * Head dimension 256 runs fwd_bf16_split_kernel instead: 8 waves per workgroup, each key tile
+//     split between two waves holding the same queries, merged at the end (see that kernel).
 #include "fa_common.h"
 #include "fa_launch.h"
 
@@ -73,9 +75,10 @@ __device__ inline void scores_tile(const char* klds, const FragOffsets<lds_cols<
 }
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void fwd_bf16_kernel(
+__global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     bf16* __restrict__ O, float* __restrict__ LSE, int N, int nqt, float scale_log2, int remap) {
+  static_assert(D <= 128, "head dimension 256 runs fwd_bf16_split_kernel");
   constexpr int KSTEPS = D / 16;  // k-steps of the Sᵀ product
   constexpr int DB = D / 32;      // 32-row blocks of Oᵀ
   constexpr int L = lds_cols<D>();
@@ -268,6 +271,199 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void fwd_bf16_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------------------------------
+// Head dimension 256: a wave's Oᵀ accumulator (32 queries × 256) and Qᵀ fragments leave no room for
+// the scores of 64 keys at two waves per SIMD, so each 64-key tile is split between two waves that
+// hold the same 32 queries: wave w (key half 0) and wave w + 4 (key half 1) each take one 32-key block
+// of every tile, keep their own reference maximum m, partial row sum l and Oᵀ, and are merged at the
+// end by softmax mass (O = (2^(m0−m) O0 + 2^(m1−m) O1) / (2^(m0−m) l0 + 2^(m1−m) l1), m = max(m0, m1):
+// the online-softmax recurrence of "Anatomy ...", section "What is online softmax and how does tiling
+// keep it exact?", applied to the two key subsets).  8 waves per workgroup, 128 queries, one
+// workgroup per CU: two waves per SIMD, each with a D = 128 wave's amount of work per tile.
+constexpr int kSplitWaves = 8;
+constexpr int kSplitThreads = 64 * kSplitWaves;
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kSplitThreads, 1) void fwd_bf16_split_kernel(
+    const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
+    bf16* __restrict__ O, float* __restrict__ LSE, int N, int nqt, float scale_log2, int remap) {
+  constexpr int KSTEPS = D / 16;
+  constexpr int DB = D / 32;
+  constexpr int L = lds_cols<D>();
+  // K(j), V(j) live in k<j % 2>, v<j % 2>; after the key loop the four buffers carry the key-half-1
+  // waves' partial outputs to their partners (one 32 KiB buffer per query block).
+  __shared__ __attribute__((aligned(1024))) bf16 k0s[kBC * L];
+  __shared__ __attribute__((aligned(1024))) bf16 k1s[kBC * L];
+  __shared__ __attribute__((aligned(1024))) bf16 v0s[kBC * L];
+  __shared__ __attribute__((aligned(1024))) bf16 v1s[kBC * L];
+  __shared__ __attribute__((aligned(256))) float xml[4][2][64];  // key half 1: (m, l) per lane
+  static_assert(DB * 16 * 64 * 4 == kBC * L * 2, "one wave's Oᵀ fills one staging buffer");
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = wave_index(tid);
+  const int qblk = wave & 3;  // query block of the wave
+  const int kh = wave >> 2;   // key half: keys 32kh .. 32kh + 31 of every tile
+  const int g = lane >> 5;
+  const int lc = lane & 31;
+
+  const uint32_t total = gridDim.x;
+  const uint32_t logical = remap ? xcd_remap(blockIdx.x, total) : blockIdx.x;
+  const int bh = logical / nqt;
+  int qt = logical % nqt;
+  if (CAUSAL) qt = nqt - 1 - qt;
+  const int q0 = qt * kBR;
+  const int qw = q0 + qblk * 32;
+  const int qi = qw + lc;
+
+  const size_t head = (size_t)bh * N * D;
+  const uint32_t head_bytes = (uint32_t)N * D * 2u;
+  const auto rq = make_rsrc(Q + head, head_bytes);
+  const auto mk = make_rsrc(K + head, head_bytes);
+  const auto mv = make_rsrc(V + head, head_bytes);
+  const BfTileCopy<D, kBC, kSplitThreads> copy(tid);
+
+  bf16x8 qf[KSTEPS];
+#pragma unroll
+  for (int s = 0; s < KSTEPS; ++s)
+    qf[s] = __builtin_bit_cast(bf16x8, buf_load16(rq, (uint32_t)(qi * D + 16 * s + 8 * g) * 2u));
+
+  const int kv_end = CAUSAL ? min(N, q0 + kBR) : N;
+  const int ntiles = (kv_end + kBC - 1) / kBC;
+  const FragOffsets<L> fo(lane);
+
+  copy(mk, 0, k0s);
+  copy(mv, 0, v0s);
+  wait_vmem_all();
+  __syncthreads();
+
+  float m = -INFINITY;  // reference maximum of the base-2 scaled scores (slack rule as above)
+  float l = 0.f;        // partial row sum over this lane's keys of this key half
+  f32x16 oacc[DB];
+#pragma unroll
+  for (int b = 0; b < DB; ++b)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) oacc[b][r] = 0.f;
+
+  auto tile = [&](auto parity, int j) {
+    constexpr int P = decltype(parity)::value;
+    if (j + 1 < ntiles) {
+      copy(mk, (j + 1) * kBC, P ? k0s : k1s);
+      copy(mv, (j + 1) * kBC, P ? v0s : v1s);
+    }
+    const char* klds = (const char*)(P ? k1s : k0s);
+    const char* vlds = (const char*)(P ? v1s : v0s);
+    const int kb0 = j * kBC + 32 * kh;  // first key of this wave's block
+    if (!(CAUSAL && kb0 > qw + 31) && kb0 < N) {
+      // Sᵀ for the block: element r is key kb0 + 8(r/4) + 4g + (r%4) for query qi.
+      f32x16 sacc;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
+#pragma unroll
+      for (int s = 0; s < KSTEPS; ++s) sacc = mfma_32x32x16(row_frag<L>(klds, fo, kh, s), qf[s], sacc);
+      if ((kb0 + 32 > N) || (CAUSAL && kb0 + 31 > qw)) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = kb0 + 8 * (r >> 2) + 4 * g + (r & 3);
+          if (key >= N || (CAUSAL && key > qi)) sacc[r] = -INFINITY;
+        }
+      }
+      float mx = sacc[0];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sacc[r]);
+      const float mt = halves_max(mx) * scale_log2;
+      if (!wave_all(mt <= m + kSlack)) {
+        const float m_new = fmaxf(m, mt);
+        const float alpha = exp2_fast(m - (m_new == -INFINITY ? 0.f : m_new));
+        l *= alpha;
+#pragma unroll
+        for (int b = 0; b < DB; ++b)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[b][r] *= alpha;
+        m = m_new;
+      }
+      const float m_use = (m == -INFINITY) ? 0.f : m;
+      // Pᵀ operand: k-step ks (16 keys) takes registers 8ks .. 8ks + 7, keys 16ks + 8(e/4) + 4g +
+      // (e%4) of the block — the order of the transposed V reads of rows 32kh + 16ks + ...
+      bf16x8 pf[2];
+      float rs[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float p = exp2_fast(fmaf(sacc[8 * ks + e], scale_log2, -m_use));
+          rs[e & 3] += p;
+          pf[ks][e] = (__bf16)p;
+        }
+      l += (rs[0] + rs[1]) + (rs[2] + rs[3]);
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int b = 0; b < DB; ++b)
+          oacc[b] = mfma_32x32x16(tr_frag<L>(vlds, fo, 2 * kh + ks, b), pf[ks], oacc[b]);
+    }
+    wait_vmem_all();
+    __syncthreads();
+  };
+
+  for (int j = 0; j < ntiles; j += 2) {
+    tile(std::integral_constant<int, 0>{}, j);
+    if (j + 1 < ntiles) tile(std::integral_constant<int, 1>{}, j + 1);
+  }
+
+  // Merge the key halves (every wave has passed the last barrier, so the K/V buffers are free).
+  float* xo = (float*)(qblk == 0 ? k0s : qblk == 1 ? k1s : qblk == 2 ? v0s : v1s);
+  if (kh == 1) {
+#pragma unroll
+    for (int b = 0; b < DB; ++b)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) xo[(b * 16 + r) * 64 + lane] = oacc[b][r];
+    xml[qblk][0][lane] = m;
+    xml[qblk][1][lane] = l;
+  }
+  __syncthreads();
+  if (kh == 0) {
+    const float m1 = xml[qblk][0][lane];
+    const float l1 = xml[qblk][1][lane];
+    // Key half 0 always holds key 0 of the row (causal) or a full block, so m is finite here for
+    // every row with an unmasked key; half 1 may have seen none (m1 = −inf, l1 = 0).
+    const float mm = fmaxf(m, m1);
+    const float a0 = exp2_fast(m - mm);
+    const float a1 = (m1 == -INFINITY) ? 0.f : exp2_fast(m1 - mm);
+    const float l_tot = halves_sum(a0 * l + a1 * l1);
+    const float inv = 1.f / l_tot;
+    const float w0 = a0 * inv, w1 = a1 * inv;
+    if (qi < N) {
+      bf16* orow = O + head + (size_t)qi * D;
+#pragma unroll
+      for (int b = 0; b < DB; ++b)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          float o4[4];
+#pragma unroll
+          for (int t = 0; t < 4; ++t)
+            o4[t] = oacc[b][4 * r4 + t] * w0 + xo[(b * 16 + 4 * r4 + t) * 64 + lane] * w1;
+          u32x2 w;
+          w[0] = pack_bf16x2(o4[0], o4[1]);
+          w[1] = pack_bf16x2(o4[2], o4[3]);
+          *(u32x2*)&orow[32 * b + 8 * r4 + 4 * g] = w;
+        }
+      if (g == 0) LSE[(size_t)bh * N + qi] = (mm + __log2f(l_tot)) * kLn2;
+    }
+  }
+}
+
+template <bool CAUSAL>
+hipError_t launch_split(const FwdArgs& a, hipStream_t stream) {
+  const int nqt = (a.N + kBR - 1) / kBR;
+  const uint32_t total = (uint32_t)a.B * a.H * nqt;
+  const int remap = (total % 8u == 0u) ? 1 : 0;
+  hipLaunchKernelGGL((fwd_bf16_split_kernel<256, CAUSAL>), dim3(total), dim3(kSplitThreads), 0,
+                     stream, (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, (bf16*)a.o, a.lse,
+                     a.N, nqt, a.scale * kLog2e, remap);
+  return hipGetLastError();
+}
+
 template <int D, bool CAUSAL>
 hipError_t launch(const FwdArgs& a, hipStream_t stream) {
   const int nqt = (a.N + kBR - 1) / kBR;
@@ -285,7 +481,7 @@ hipError_t launch(const FwdArgs& a, hipStream_t stream) {
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream) {
   if (a.d == 64) return a.causal ? launch<64, true>(a, stream) : launch<64, false>(a, stream);
   if (a.d == 96) return a.causal ? launch<96, true>(a, stream) : launch<96, false>(a, stream);
-  if (a.d == 256) return a.causal ? launch<256, true>(a, stream) : launch<256, false>(a, stream);
+  if (a.d == 256) return a.causal ? launch_split<true>(a, stream) : launch_split<false>(a, stream);
   return a.causal ? launch<128, true>(a, stream) : launch<128, false>(a, stream);
 }
 
