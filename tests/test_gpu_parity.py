@@ -305,6 +305,34 @@ def test_wide_heads_many_tiles(d, causal):
     _check_bwd_heads(q, k, v, do, dq.cpu(), dk.cpu(), dv.cpu(), causal, scale, range(B * H))
 
 
+def test_concurrent_streams_match_sequential():
+    """Calls on two streams at once (default priority) give bitwise what the same calls give one
+    after another: the library keeps no state between calls and each call owns its workspace."""
+    g = torch.Generator().manual_seed(77)
+    shapes = [(2, 3, 700, 128), (1, 4, 513, 64)]
+    ins = [[torch.randn(*sh, generator=g).to(torch.bfloat16).cuda() for _ in range(4)] for sh in shapes]
+
+    def work(q, k, v, do):
+        o, lse = fa().fwd(q, k, v, True)
+        grads = fa().bwd(q, k, v, o, lse, do, True)
+        od, ld = fa().decode(q[:, :, -5:].contiguous(), k, v, True)
+        return [o, lse, *grads, od, ld]
+
+    seq = [work(*x) for x in ins]
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream() for _ in ins]
+    outs = [None, None]
+    for _ in range(3):
+        for i, (st, x) in enumerate(zip(streams, ins)):
+            st.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(st):
+                outs[i] = work(*x)
+        torch.cuda.synchronize()
+        for got, want in zip(outs, seq):
+            for a, b in zip(got, want):
+                assert torch.equal(a, b)
+
+
 @pytest.mark.parametrize("scale", [0.03, 0.4])
 @pytest.mark.parametrize("d", [64, 96, 128])
 def test_fwd_bwd_other_softmax_scales(scale, d):
