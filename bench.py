@@ -17,6 +17,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -35,12 +36,21 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def _code_text(path):
+    """A source file's code without comments and blank lines: edits to comments leave it unchanged."""
+    with open(path, encoding="utf-8") as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    lines = (re.sub(r"//.*$", "", ln).rstrip() for ln in text.splitlines())
+    return "\n".join(ln for ln in lines if ln)
+
+
 def source_sha(name):
-    """sha256 prefix over a kernel's source file and the device headers every kernel includes."""
+    """sha256 prefix over the code (not the comments) of a kernel's source file and of the device
+    headers every kernel includes."""
     h = hashlib.sha256()
     for part in (name, "fa_common.h", "fa_launch.h"):
-        with open(os.path.join(ROOT, "io_aware_exact_18_amd", "csrc", part), "rb") as f:
-            h.update(f.read())
+        h.update(_code_text(os.path.join(ROOT, "io_aware_exact_18_amd", "csrc", part)).encode())
     return h.hexdigest()[:16]
 
 

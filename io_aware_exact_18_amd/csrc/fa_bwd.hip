@@ -13,13 +13,15 @@
 //   2. bwd_dkdv: key/value-stationary.  One workgroup per 128 keys (4 waves × 32 keys).  Each wave
 //      keeps its K rows as matrix-core operands and its dKᵀ, dVᵀ accumulators in registers (V rows
 //      stay in LDS) and walks the 32-query tiles the causal mask allows, staged in LDS by direct
-//      buffer→LDS copies (double-buffered, one barrier per tile).  Per tile: S = Q Kᵀ and dP = dO Vᵀ (32×32×16 bf16
-//      matrix cores, Q and dO rows from LDS), P and dS on the vector units, then dVᵀ += dOᵀ P and
-//      dKᵀ += Qᵀ dS with transposed LDS reads supplying dOᵀ and Qᵀ.
+//      buffer→LDS copies (double-buffered, one barrier per tile).  Per tile: S = Q Kᵀ and
+//      dP = dO Vᵀ (32×32×16 bf16 matrix cores, Q and dO rows from LDS), P and dS on the vector
+//      units, then dVᵀ += dOᵀ P and dKᵀ += Qᵀ dS with transposed LDS reads supplying dOᵀ and Qᵀ.
+//      At head dimension 256 it runs as two passes, dV then dK (see the kernel).
 //   3. bwd_dq: query-stationary, the same shape as the forward: one workgroup per 128 queries
 //      (4 waves × 32), key/value tiles of 64 streamed through LDS.  Per tile it recomputes Sᵀ = K Qᵀ
 //      and dPᵀ = V dOᵀ (each lane owns one query, so LSE_i and D_i are per-lane scalars), forms dSᵀ,
 //      and accumulates dQᵀ += Kᵀ dSᵀ with K read transposed from LDS.
+// Head dimension 96 keeps its tiles in the d = 128 LDS layout (lds_cols in fa_common.h).
 // Splitting dQ off costs two recomputed products (7 matrix products executed for the 5 counted) but
 // removes the fp32 atomics a single-kernel dQ would need: measured on MI355X, device-wide fp32 atomic
 // adds sustain about 1.3 TB/s, which for the 4096-token causal workload alone would take ~3 ms.
