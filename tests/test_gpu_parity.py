@@ -13,6 +13,7 @@ head is checked with size-independent properties instead.
 
 import math
 import random
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 import pytest
@@ -69,16 +70,24 @@ def _run_fwd(q, k, v, causal, scale):
     return o, lse
 
 
+def _oracle_heads(fn, heads):
+    """fn(h) for every head, four at a time (numpy releases the interpreter lock in its kernels)."""
+    with ThreadPoolExecutor(4) as ex:
+        return list(zip(heads, ex.map(fn, heads)))
+
+
 def _check_fwd_heads(q, k, v, o, lse, causal, scale, heads=None, o_tol=None):
     B, H, N, d = q.shape
-    heads = range(B * H) if heads is None else heads
+    heads = list(range(B * H) if heads is None else heads)
     qf, kf, vf = (x.reshape(B * H, N, d) for x in (q, k, v))
     of = o.reshape(B * H, N, d)
     lf = lse.reshape(B * H, N)
     worst_o = worst_l = 0.0
-    for h in heads:
-        o_ref, l_ref = oracle.attention_head_fwd64(_np64(qf[h]), _np64(kf[h]), _np64(vf[h]),
-                                                   causal, scale)
+
+    def ref(h):
+        return oracle.attention_head_fwd64(_np64(qf[h]), _np64(kf[h]), _np64(vf[h]), causal, scale)
+
+    for h, (o_ref, l_ref) in _oracle_heads(ref, heads):
         og, lg = _np64(of[h]), _np64(lf[h])
         assert np.all(np.isfinite(og)) and np.all(np.isfinite(lg))
         err = np.abs(og - o_ref)
@@ -401,17 +410,20 @@ def test_workload_reduced(name):
 
 @pytest.mark.parametrize("name", ["d64_2k", "causal_4k", "d256_4k", "d96_4k"])
 def test_workload_full(name):
-    """Full size, as the bench runs it: sampled heads against the oracle, properties on all heads."""
+    """Full size, as the bench runs it: the forward of every head against the oracle, the backward
+    of sampled heads, and the backward's exact sums on all heads."""
     w = workloads.WORKLOADS[name]
     inp = workloads.make_inputs(name)
     o, lse, dq, dk, dv = _run_bwd(inp["q"], inp["k"], inp["v"], inp["do"], w.causal, w.scale)
     for t in (o, lse, dq, dk, dv):
         assert bool(torch.isfinite(t).all())
-    heads = _sample_heads(w.B * w.H, 4, seed=w.number)
+    # Causal rows near the start see only a few keys, so |O| reaches 2-4 there, where storing O in
+    # bf16 alone costs up to 1/64: those workloads take the bound 1e-2 + half a bf16 ulp of O*.
     _check_fwd_heads(inp["q"], inp["k"], inp["v"], o.cpu(), lse.cpu(), w.causal, w.scale,
-                     heads=heads)
+                     o_tol="bf16_store" if w.causal else None)
+    heads = _sample_heads(w.B * w.H, 4, seed=w.number)
     _check_bwd_heads(inp["q"], inp["k"], inp["v"], inp["do"], dq.cpu(), dk.cpu(), dv.cpu(),
-                     w.causal, w.scale, heads[:2])
+                     w.causal, w.scale, heads)
     _check_bwd_sums(inp["do"], dk, dv)
 
 
@@ -516,9 +528,12 @@ def _check_fp8_heads(inp, o, lse, causal, scale, heads):
     qf, kf, vf = (x.reshape(B * H, N, d) for x in (q, k, v))
     of, lf = o.reshape(B * H, N, d), lse.reshape(B * H, N)
     worst_o = worst_l = 0.0
-    for h in heads:
-        o_ref, l_ref = oracle.attention_head_fwd64(qf[h].numpy(), kf[h].numpy(), vf[h].numpy(),
-                                                   causal, scale)
+
+    def ref(h):
+        return oracle.attention_head_fwd64(qf[h].numpy(), kf[h].numpy(), vf[h].numpy(), causal,
+                                           scale)
+
+    for h, (o_ref, l_ref) in _oracle_heads(ref, list(heads)):
         og, lg = _np64(of[h]), _np64(lf[h])
         assert np.all(np.isfinite(og)) and np.all(np.isfinite(lg))
         e_o = float(np.abs(og - o_ref).max())
@@ -557,14 +572,15 @@ def test_fp8_workload_reduced():
 
 
 def test_fp8_workload_full():
-    """fp8_8k at full size: sampled heads in full against the oracle; in every head, the first 96
-    rows (few keys: the rows where rounding P to e4m3 moves O the most) and 16 random rows, each
-    computed on its own by the oracle; every output finite."""
+    """fp8_8k at full size: every head in full against the oracle (worst O error measured 0.0506
+    against the 6e-2 bound); in every head, the first 96 rows (few keys: the rows where rounding P
+    to e4m3 moves O the most) and 16 random rows, each computed on its own by the oracle; every
+    output finite."""
     w = workloads.WORKLOADS["fp8_8k"]
     inp = workloads.make_inputs("fp8_8k")
     o, lse = _run_fp8(inp, w.causal, w.scale)
     assert bool(torch.isfinite(o.float()).all()) and bool(torch.isfinite(lse).all())
-    _check_fp8_heads(inp, o, lse, w.causal, w.scale, _sample_heads(w.B * w.H, 4, seed=w.number))
+    _check_fp8_heads(inp, o, lse, w.causal, w.scale, range(w.B * w.H))
     B, H, N, d = w.shape()
     q, k, v = (workloads.dequantized64(inp[n + "8"], inp["s" + n]).reshape(B * H, N, d)
                for n in ("q", "k", "v"))
