@@ -29,6 +29,16 @@ METRIC = "attention TFLOP/s fwd+bwd (bf16, d=128, N=4096 causal) and % of MFMA p
 BF16_PEAK_TFLOPS = 256 * 2.4e9 * 4096 / 1e12     # 2516.6
 FP8_PEAK_TFLOPS = 2 * BF16_PEAK_TFLOPS            # 5033.2 (dense e4m3 matrix cores)
 HBM_PEAK_GBS = 8000.0
+# Published figures of the method on other hardware, for workloads the source does not state
+# ("Anatomy of a FlashAttention Kernel", section "What changed between FlashAttention 1, 2, and 3?").
+# Context only: none is for this metric and workload, so vs_baseline stays null.
+PAGES_FIGURES = {
+    "flashattention2_a100_fraction_of_peak": [0.50, 0.73],
+    "flashattention3_h100_fp16_tflops": 740.0,
+    "flashattention3_h100_fp16_fraction_of_peak": 0.75,
+    "flashattention3_h100_fp8_tflops_about": 1200.0,
+    "workloads": "not stated",
+}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
@@ -628,6 +638,7 @@ def main():
         "device": device,
         "secondary": secondary,
         "cpu_baseline": cpu,
+        "context": PAGES_FIGURES,
     }
     print(json.dumps(out), flush=True)
 
