@@ -268,10 +268,11 @@ def decode_measure(fa, workloads, lib, steps, warmup):
     return out
 
 
-def fp8_forward(fa, workloads, lib, steps, warmup):
-    """Secondary measurement: the FP8 forward on its workload (fp8_8k), timed with events."""
+def fp8_forward(fa, workloads, lib, steps, warmup, name="fp8_8k"):
+    """Secondary measurement: the FP8 forward on an fp8 workload (fp8_8k; fp8_d64_8k and fp8_d96_8k
+    at the other head dimensions), timed with events."""
     import torch
-    w = workloads.WORKLOADS["fp8_8k"]
+    w = workloads.WORKLOADS[name]
     B, H, N, d = w.shape()
     log(f"[bench] secondary: {w.name} fp8 forward B={B} H={H} N={N} d={d} causal={w.causal}")
     inp = workloads.make_inputs(w.name)
@@ -598,6 +599,10 @@ def main():
         for name in ("d256_4k", "d96_4k"):
             secondary[name + "_fwd_bwd"] = fwd_bwd_secondary(fa, workloads, lib, name, args.steps,
                                                              args.warmup)
+        if not args.no_fp8:
+            for name in ("fp8_d64_8k", "fp8_d96_8k"):
+                secondary[name + "_fwd"] = fp8_forward(fa, workloads, lib, args.steps, args.warmup,
+                                                       name)
     if not args.no_configs:
         for name in ("d64_2k", "long_16k"):
             secondary[name + "_fwd_bwd"] = fwd_bwd_secondary(fa, workloads, lib, name, args.steps,

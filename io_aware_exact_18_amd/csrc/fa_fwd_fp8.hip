@@ -1,4 +1,5 @@
-// fa_fwd_fp8.hip — forward kernel with FP8 (OCP e4m3fn) matrix products for gfx950, head dim 128.
+// fa_fwd_fp8.hip — forward kernel with FP8 (OCP e4m3fn) matrix products for gfx950, head dims 64,
+// 96 and 128.
 //
 // Same method as the bf16 forward ("Anatomy of a FlashAttention Kernel", sections "Why is attention
 // memory-bound ..." and "What is online softmax ..."), with the low-precision FP8 products that the
@@ -20,6 +21,9 @@
 //     go straight from the score accumulator into the B operand.
 //   * Tiles: 4 waves × 32 queries per workgroup, 64-key K/V tiles copied into LDS by buffer→LDS DMA,
 //     K one tile ahead of V, double-buffered, rows XOR-swizzled for conflict-free reads.
+//   * Head dims: Sᵀ takes D/64 k-steps of 64, Oᵀ D/32 column blocks of 32.  d = 96 uses the d = 128
+//     LDS rows: the DMA fills bytes 96..127 of each K and V row with zeros and the Q operand's last
+//     32 columns are zero, so the second k-step adds nothing, and only three V column blocks are read.
 #include "fa_common.h"
 #include "fa_launch.h"
 
@@ -28,11 +32,12 @@
 namespace fa {
 namespace {
 
-constexpr int kD = 128;
 constexpr int kBR = 128;
 constexpr int kBC = 64;
 constexpr int kThreads = 256;
-constexpr int kRowBytes = kD;  // one e4m3 byte per element
+// Bytes per K/V row in LDS (one e4m3 byte per element; d = 96 is padded to 128).
+template <int D>
+constexpr int lds_row() { return D == 96 ? 128 : D; }
 // P is formed as 2^(s·c − m + kPExp) against a per-row reference maximum m that is raised only when
 // some row of the wave sees a score more than kSlack above it, so P ≤ 2^(kPExp + kSlack) = 256 fits
 // e4m3 (largest finite 448) and the accumulators are rescaled on few tiles instead of most.
@@ -45,9 +50,14 @@ __device__ inline T& pick(T& a, T& b) {
   else return a;
 }
 
-// Swizzle of 16-byte chunks within a 128-byte fp8 row (64 banks; two rows per bank period): keeps
-// 16-lane row reads and 32-lane 8-byte transposed reads conflict-free.
-__device__ inline int swz8(int r) { return (((r >> 1) & 3) << 1) | ((r >> 3) & 1); }
+// Swizzle of 16-byte chunks within an fp8 row of LR bytes (64 banks of 4 bytes: two 128-byte rows
+// or four 64-byte rows per bank period): keeps 16-lane row reads and 32-lane 8-byte transposed reads
+// conflict-free.
+template <int LR>
+__device__ inline int swz8(int r) {
+  if constexpr (LR == 64) return (((r >> 2) & 1) << 1) | ((r >> 3) & 1);
+  else return (((r >> 1) & 3) << 1) | ((r >> 3) & 1);
+}
 
 // Rows 32kb + i of the A operand hold K row 32kb + perm(i): bits 2 and 3 of i swapped.
 __device__ inline int perm23(int i) { return (i & ~0xC) | ((i >> 1) & 4) | ((i << 1) & 8); }
@@ -68,15 +78,19 @@ __device__ inline uint32_t pack_e4m3x4(float p0, float p1, float p2, float p3) {
   return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, lo, true);
 }
 
-template <bool CAUSAL>
+template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 2) void fwd_fp8_kernel(
     const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K, const uint8_t* __restrict__ V,
     bf16* __restrict__ O, float* __restrict__ LSE, int N, int nqt, float c_log2, float v_descale,
     int remap) {
-  __shared__ __attribute__((aligned(1024))) uint8_t k0s[kBC * kRowBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t k1s[kBC * kRowBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t v0s[kBC * kRowBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t v1s[kBC * kRowBytes];
+  static_assert(D == 64 || D == 96 || D == 128, "head dims of the fp8 forward");
+  constexpr int LR = lds_row<D>();
+  constexpr int KS = LR / 64;  // k-steps of Sᵀ
+  constexpr int DB = D / 32;   // column blocks of Oᵀ
+  __shared__ __attribute__((aligned(1024))) uint8_t k0s[kBC * LR];
+  __shared__ __attribute__((aligned(1024))) uint8_t k1s[kBC * LR];
+  __shared__ __attribute__((aligned(1024))) uint8_t v0s[kBC * LR];
+  __shared__ __attribute__((aligned(1024))) uint8_t v1s[kBC * LR];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -92,43 +106,47 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_fp8_kernel(
   const int qw = q0 + 32 * wave;
   const int qi = qw + lc;
 
-  const size_t head = (size_t)bh * N * kD;
-  const uint32_t head_bytes = (uint32_t)N * kRowBytes;
+  const size_t head = (size_t)bh * N * D;
+  const uint32_t head_bytes = (uint32_t)N * D;
   const auto rq = make_rsrc(Q + head, head_bytes);
   const auto mk = make_rsrc(K + head, head_bytes);
   const auto mv = make_rsrc(V + head, head_bytes);
-  const TileCopy<kRowBytes, kBC, kThreads> copy(tid, [](int r) { return swz8(r); });
+  const TileCopy<LR, kBC, kThreads, D> copy(tid, [](int r) { return swz8<LR>(r); });
 
-  // Qᵀ operand (B): this lane's query, k-step s covers d = 64s + 32g .. +31.
-  i32x8 qf[2];
+  // Qᵀ operand (B): this lane's query, k-step s covers d = 64s + 32g .. +31.  Columns past D (only
+  // d = 96) read from an offset past the buffer's range, which returns zeros.
+  i32x8 qf[KS];
 #pragma unroll
-  for (int s = 0; s < 2; ++s) {
-    const uint32_t off = (uint32_t)(qi * kRowBytes + 64 * s + 32 * g);
+  for (int s = 0; s < KS; ++s) {
+    uint32_t off = (uint32_t)(qi * D + 64 * s + 32 * g);
+    if constexpr (D == 96) {
+      if (s == 1 && g == 1) off = 0x80000000u;
+    }
     const u32x4 lo = buf_load16(rq, off), hi = buf_load16(rq, off + 16);
     qf[s] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
                   (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
   }
 
   // Per-lane LDS offsets.  K rows (A operand): row perm23(lc) (+32 per key block), chunks 4s+2g+h.
-  uint32_t koff[2][2];
+  uint32_t koff[KS][2];
   {
     const int r = perm23(lc);
 #pragma unroll
-    for (int s = 0; s < 2; ++s)
+    for (int s = 0; s < KS; ++s)
 #pragma unroll
       for (int h = 0; h < 2; ++h)
-        koff[s][h] = (uint32_t)(r * kRowBytes + 16 * ((4 * s + 2 * g + h) ^ swz8(r)));
+        koff[s][h] = (uint32_t)(r * LR + 16 * ((4 * s + 2 * g + h) ^ swz8<LR>(r)));
   }
   // V transposed reads: the 16-lane group's lane i = 2a + b reads row k0 + a, bytes n0 + 8b .. +7
   // with k0 = 16c + 8g and n0 = 32db + 16·((lane >> 4) & 1); the lane receives column n0 + (i) of
   // rows k0 .. k0 + 7.  voff[db] is the offset for c = 0 (c adds 16 rows).
-  uint32_t voff[4];
+  uint32_t voff[DB];
   {
     const int a = (lane & 15) >> 1, b = lane & 1, u = (lane >> 4) & 1;
     const int r = 8 * g + a;
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
-      voff[db] = (uint32_t)(r * kRowBytes + 16 * ((2 * db + u) ^ swz8(r)) + 8 * b);
+    for (int db = 0; db < DB; ++db)
+      voff[db] = (uint32_t)(r * LR + 16 * ((2 * db + u) ^ swz8<LR>(r)) + 8 * b);
   }
 
   const int kv_end = CAUSAL ? min(N, q0 + kBR) : N;
@@ -147,9 +165,9 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_fp8_kernel(
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[kb][r] = 0.f;
 #pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        const u32x4 lo = *(const u32x4*)(klds + koff[s][0] + kb * 32 * kRowBytes);
-        const u32x4 hi = *(const u32x4*)(klds + koff[s][1] + kb * 32 * kRowBytes);
+      for (int s = 0; s < KS; ++s) {
+        const u32x4 lo = *(const u32x4*)(klds + koff[s][0] + kb * 32 * LR);
+        const u32x4 hi = *(const u32x4*)(klds + koff[s][1] + kb * 32 * LR);
         const i32x8 kf = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
                           (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
         acc[kb] = mfma_f8(kf, qf[s], acc[kb]);
@@ -162,9 +180,9 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_fp8_kernel(
   __syncthreads();
 
   float m = -INFINITY;
-  f32x16 oacc[4], lacc;
+  f32x16 oacc[DB], lacc;
 #pragma unroll
-  for (int b = 0; b < 4; ++b)
+  for (int b = 0; b < DB; ++b)
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[b][r] = 0.f;
 #pragma unroll
@@ -207,7 +225,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_fp8_kernel(
         const float m_new = fmaxf(m, mt);
         const float alpha = exp2_fast(m - (m_new == -INFINITY ? 0.f : m_new));
 #pragma unroll
-        for (int b = 0; b < 4; ++b)
+        for (int b = 0; b < DB; ++b)
 #pragma unroll
           for (int r = 0; r < 16; ++r) oacc[b][r] *= alpha;
 #pragma unroll
@@ -237,11 +255,11 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_fp8_kernel(
 
       // Oᵀ += Vᵀ Pᵀ: A operand = V column 32db + lc, keys in the order of P's bytes.
 #pragma unroll
-      for (int db = 0; db < 4; ++db) {
+      for (int db = 0; db < DB; ++db) {
         i32x8 vf;
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-          const u32x2 t8 = lds_read_tr8(v_this + voff[db] + c * 16 * kRowBytes);
+          const u32x2 t8 = lds_read_tr8(v_this + voff[db] + c * 16 * LR);
           vf[2 * c] = (int)t8[0];
           vf[2 * c + 1] = (int)t8[1];
         }
@@ -261,9 +279,9 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_fp8_kernel(
   const float l = lacc[0];
   const float inv = v_descale / l;
   if (qi < N) {
-    bf16* orow = O + head + (size_t)qi * kD;
+    bf16* orow = O + head + (size_t)qi * D;
 #pragma unroll
-    for (int b = 0; b < 4; ++b)
+    for (int b = 0; b < DB; ++b)
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
         u32x2 w;
@@ -275,13 +293,13 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_fp8_kernel(
   }
 }
 
-template <bool CAUSAL>
+template <int D, bool CAUSAL>
 hipError_t launch(const Fp8FwdArgs& a, hipStream_t stream) {
   const int nqt = (a.N + kBR - 1) / kBR;
   const uint32_t total = (uint32_t)a.B * a.H * nqt;
   const int remap = (total % 8u == 0u) ? 1 : 0;
   const float c_log2 = a.scale * a.q_descale * a.k_descale * kLog2e;
-  hipLaunchKernelGGL((fwd_fp8_kernel<CAUSAL>), dim3(total), dim3(kThreads), 0, stream,
+  hipLaunchKernelGGL((fwd_fp8_kernel<D, CAUSAL>), dim3(total), dim3(kThreads), 0, stream,
                      (const uint8_t*)a.q8, (const uint8_t*)a.k8, (const uint8_t*)a.v8, (bf16*)a.o,
                      a.lse, a.N, nqt, c_log2, a.v_descale, remap);
   return hipGetLastError();
@@ -289,8 +307,18 @@ hipError_t launch(const Fp8FwdArgs& a, hipStream_t stream) {
 
 }  // namespace
 
+template <int D>
+hipError_t launch_d(const Fp8FwdArgs& a, hipStream_t stream) {
+  return a.causal ? launch<D, true>(a, stream) : launch<D, false>(a, stream);
+}
+
 hipError_t launch_fwd_fp8(const Fp8FwdArgs& a, hipStream_t stream) {
-  return a.causal ? launch<true>(a, stream) : launch<false>(a, stream);
+  switch (a.d) {
+    case 64: return launch_d<64>(a, stream);
+    case 96: return launch_d<96>(a, stream);
+    case 128: return launch_d<128>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace fa

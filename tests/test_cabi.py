@@ -78,7 +78,7 @@ def test_fwd_rejections(lib):
     assert fwd(lib, H=-1) == SHAPE
     assert fwd(lib, N=0) == SHAPE
     assert fwd(lib, d=80) == UNSUP
-    assert fwd8(lib, d=96) == UNSUP
+    assert fwd8(lib, d=32) == UNSUP
     assert fwd(lib, d=32) == UNSUP
     assert fwd(lib, d=512) == UNSUP
     assert fwd8(lib, d=256) == UNSUP
@@ -96,7 +96,8 @@ def fwd8(lib, d=128, qs=1.0, ks=1.0, vs=1.0, k8=P, scale=0.09):
 
 def test_fwd_fp8_rejections(lib):
     assert fwd8(lib, k8=None) == NULL
-    assert fwd8(lib, d=64) == UNSUP
+    assert fwd8(lib, d=256) == UNSUP                    # fp8 forward: d ∈ {64, 96, 128}
+    assert fwd8(lib, d=80) == UNSUP
     assert fwd8(lib, qs=0.0) == UNSUP
     assert fwd8(lib, vs=math.nan) == UNSUP
     assert fwd8(lib, scale=-1.0) == UNSUP
