@@ -269,8 +269,8 @@ def decode_measure(fa, workloads, lib, steps, warmup):
 
 
 def fp8_forward(fa, workloads, lib, steps, warmup, name="fp8_8k"):
-    """Secondary measurement: the FP8 forward on an fp8 workload (fp8_8k; fp8_d64_8k and fp8_d96_8k
-    at the other head dimensions), timed with events."""
+    """Secondary measurement: the FP8 forward on an fp8 workload (fp8_8k; fp8_d64_8k, fp8_d96_8k and
+    fp8_d256_8k at the other head dimensions), timed with events."""
     import torch
     w = workloads.WORKLOADS[name]
     B, H, N, d = w.shape()
@@ -600,7 +600,7 @@ def main():
             secondary[name + "_fwd_bwd"] = fwd_bwd_secondary(fa, workloads, lib, name, args.steps,
                                                              args.warmup)
         if not args.no_fp8:
-            for name in ("fp8_d64_8k", "fp8_d96_8k"):
+            for name in ("fp8_d64_8k", "fp8_d96_8k", "fp8_d256_8k"):
                 secondary[name + "_fwd"] = fp8_forward(fa, workloads, lib, args.steps, args.warmup,
                                                        name)
     if not args.no_configs:

@@ -18,8 +18,8 @@
  *  LSE        LSE_i = ln Σ_j exp(scale · q_i·k_j) over the keys query i may use: natural log of the
  *             scaled scores.  It stands for the pair (row maximum, softmax denominator).
  *  Causal     causal != 0 lets query i use key j only when j ≤ i; causal == 0 lets it use all keys.
- *  Supported  d ∈ {64, 96, 128, 256} (fa_fwd_fp8: d ∈ {64, 96, 128}); N ≥ 1; B, H ≥ 1; B·H·N·d < 2^40.  bf16
- *             values are IEEE bfloat16.
+ *  Supported  d ∈ {64, 96, 128, 256}; N ≥ 1; B, H ≥ 1; B·H·N·d < 2^40.  bf16 values are IEEE
+ *             bfloat16.
  *  Memory     Every pointer is a device pointer owned by the caller and 16-byte aligned.  The library
  *             never allocates or frees device memory and keeps no state between calls.
  *  Streams    Every call only enqueues work on `stream` and returns; results are ready when the stream
@@ -68,7 +68,6 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
  *   q8, k8, v8   [B,H,N,d] e4m3fn codes (1 byte each), 16-byte aligned.
  *   q_descale, k_descale, v_descale   finite, > 0.
  *   o            [B,H,N,d] bf16 output;  lse  [B,H,N] fp32 output (natural log, scaled scores).
- * d ∈ {64, 96, 128}; d = 256 returns FA_ERR_UNSUPPORTED.
  */
 fa_status fa_fwd_fp8(const void* q8, const void* k8, const void* v8,
                      float q_descale, float k_descale, float v_descale, void* o, float* lse,

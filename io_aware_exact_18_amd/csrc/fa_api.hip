@@ -72,7 +72,6 @@ fa_status fa_fwd_fp8(const void* q8, const void* k8, const void* v8, float q_des
   if (!q8 || !k8 || !v8 || !o || !lse) return FA_ERR_NULL;
   fa_status st = check_shape(B, H, N, d, 2);
   if (st != FA_OK) return st;
-  if (d == 256) return FA_ERR_UNSUPPORTED;
   if (!good_scale(softmax_scale) || !good_scale(q_descale) || !good_scale(k_descale) ||
       !good_scale(v_descale))
     return FA_ERR_UNSUPPORTED;

@@ -1,5 +1,5 @@
 // fa_fwd_fp8.hip — forward kernel with FP8 (OCP e4m3fn) matrix products for gfx950, head dims 64,
-// 96 and 128.
+// 96, 128 and 256.
 //
 // Same method as the bf16 forward ("Anatomy of a FlashAttention Kernel", sections "Why is attention
 // memory-bound ..." and "What is online softmax ..."), with the low-precision FP8 products that the
@@ -24,6 +24,10 @@
 //   * Head dims: Sᵀ takes D/64 k-steps of 64, Oᵀ D/32 column blocks of 32.  d = 96 uses the d = 128
 //     LDS rows: the DMA fills bytes 96..127 of each K and V row with zeros and the Q operand's last
 //     32 columns are zero, so the second k-step adds nothing, and only three V column blocks are read.
+//   * d = 256: two workgroups per query tile, one per 128-column half of O.  Each forms the full Sᵀ
+//     (four k-steps) and the same P, and accumulates only its half of Oᵀ, so the state per wave stays
+//     that of d = 128.  Sᵀ is computed twice: 1.5× the matrix-core work of one pass.  The two halves
+//     are adjacent work items, so they run on one XCD and share its L2 for K and V.
 #include "fa_common.h"
 #include "fa_launch.h"
 
@@ -38,6 +42,9 @@ constexpr int kThreads = 256;
 // Bytes per K/V row in LDS (one e4m3 byte per element; d = 96 is padded to 128).
 template <int D>
 constexpr int lds_row() { return D == 96 ? 128 : D; }
+// Workgroups per query tile (column halves of O).
+template <int D>
+constexpr int col_splits() { return D == 256 ? 2 : 1; }
 // P is formed as 2^(s·c − m + kPExp) against a per-row reference maximum m that is raised only when
 // some row of the wave sees a score more than kSlack above it, so P ≤ 2^(kPExp + kSlack) = 256 fits
 // e4m3 (largest finite 448) and the accumulators are rescaled on few tiles instead of most.
@@ -50,12 +57,13 @@ __device__ inline T& pick(T& a, T& b) {
   else return a;
 }
 
-// Swizzle of 16-byte chunks within an fp8 row of LR bytes (64 banks of 4 bytes: two 128-byte rows
-// or four 64-byte rows per bank period): keeps 16-lane row reads and 32-lane 8-byte transposed reads
-// conflict-free.
+// Swizzle of 16-byte chunks within an fp8 row of LR bytes (64 banks of 4 bytes: one 256-byte row,
+// two 128-byte rows or four 64-byte rows per bank period): keeps 16-lane row reads and 32-lane 8-byte
+// transposed reads conflict-free.
 template <int LR>
 __device__ inline int swz8(int r) {
   if constexpr (LR == 64) return (((r >> 2) & 1) << 1) | ((r >> 3) & 1);
+  else if constexpr (LR == 256) return ((r & 7) << 1) | ((r >> 3) & 1);
   else return (((r >> 1) & 3) << 1) | ((r >> 3) & 1);
 }
 
@@ -83,10 +91,10 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_fp8_kernel(
     const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K, const uint8_t* __restrict__ V,
     bf16* __restrict__ O, float* __restrict__ LSE, int N, int nqt, float c_log2, float v_descale,
     int remap) {
-  static_assert(D == 64 || D == 96 || D == 128, "head dims of the fp8 forward");
+  static_assert(D == 64 || D == 96 || D == 128 || D == 256, "head dims of the fp8 forward");
   constexpr int LR = lds_row<D>();
-  constexpr int KS = LR / 64;  // k-steps of Sᵀ
-  constexpr int DB = D / 32;   // column blocks of Oᵀ
+  constexpr int KS = LR / 64;                   // k-steps of Sᵀ
+  constexpr int DB = D / 32 / col_splits<D>();  // column blocks of Oᵀ per workgroup
   __shared__ __attribute__((aligned(1024))) uint8_t k0s[kBC * LR];
   __shared__ __attribute__((aligned(1024))) uint8_t k1s[kBC * LR];
   __shared__ __attribute__((aligned(1024))) uint8_t v0s[kBC * LR];
@@ -99,8 +107,10 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_fp8_kernel(
   const int lc = lane & 31;
 
   const uint32_t logical = remap ? xcd_remap(blockIdx.x, gridDim.x) : blockIdx.x;
-  const int bh = logical / nqt;
-  int qt = logical % nqt;
+  const int half = col_splits<D>() == 2 ? (int)(logical & 1u) : 0;  // column half of O (d = 256)
+  const uint32_t item = col_splits<D>() == 2 ? logical >> 1 : logical;
+  const int bh = item / nqt;
+  int qt = item % nqt;
   if (CAUSAL) qt = nqt - 1 - qt;
   const int q0 = qt * kBR;
   const int qw = q0 + 32 * wave;
@@ -138,15 +148,15 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_fp8_kernel(
         koff[s][h] = (uint32_t)(r * LR + 16 * ((4 * s + 2 * g + h) ^ swz8<LR>(r)));
   }
   // V transposed reads: the 16-lane group's lane i = 2a + b reads row k0 + a, bytes n0 + 8b .. +7
-  // with k0 = 16c + 8g and n0 = 32db + 16·((lane >> 4) & 1); the lane receives column n0 + (i) of
-  // rows k0 .. k0 + 7.  voff[db] is the offset for c = 0 (c adds 16 rows).
+  // with k0 = 16c + 8g and n0 = 128·half + 32db + 16·((lane >> 4) & 1); the lane receives column
+  // n0 + (i) of rows k0 .. k0 + 7.  voff[db] is the offset for c = 0 (c adds 16 rows).
   uint32_t voff[DB];
   {
     const int a = (lane & 15) >> 1, b = lane & 1, u = (lane >> 4) & 1;
     const int r = 8 * g + a;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
-      voff[db] = (uint32_t)(r * LR + 16 * ((2 * db + u) ^ swz8<LR>(r)) + 8 * b);
+      voff[db] = (uint32_t)(r * LR + 16 * ((2 * (db + DB * half) + u) ^ swz8<LR>(r)) + 8 * b);
   }
 
   const int kv_end = CAUSAL ? min(N, q0 + kBR) : N;
@@ -279,7 +289,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_fp8_kernel(
   const float l = lacc[0];
   const float inv = v_descale / l;
   if (qi < N) {
-    bf16* orow = O + head + (size_t)qi * D;
+    bf16* orow = O + head + (size_t)qi * D + 32 * DB * half;
 #pragma unroll
     for (int b = 0; b < DB; ++b)
 #pragma unroll
@@ -289,14 +299,14 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_fp8_kernel(
         w[1] = pack_bf16x2(oacc[b][4 * r4 + 2] * inv, oacc[b][4 * r4 + 3] * inv);
         *(u32x2*)&orow[32 * b + 8 * r4 + 4 * g] = w;
       }
-    if (g == 0) LSE[(size_t)bh * N + qi] = (m - kPExp + __log2f(l)) * kLn2;
+    if (g == 0 && half == 0) LSE[(size_t)bh * N + qi] = (m - kPExp + __log2f(l)) * kLn2;
   }
 }
 
 template <int D, bool CAUSAL>
 hipError_t launch(const Fp8FwdArgs& a, hipStream_t stream) {
   const int nqt = (a.N + kBR - 1) / kBR;
-  const uint32_t total = (uint32_t)a.B * a.H * nqt;
+  const uint32_t total = (uint32_t)a.B * a.H * nqt * col_splits<D>();
   const int remap = (total % 8u == 0u) ? 1 : 0;
   const float c_log2 = a.scale * a.q_descale * a.k_descale * kLog2e;
   hipLaunchKernelGGL((fwd_fp8_kernel<D, CAUSAL>), dim3(total), dim3(kThreads), 0, stream,
@@ -317,6 +327,7 @@ hipError_t launch_fwd_fp8(const Fp8FwdArgs& a, hipStream_t stream) {
     case 64: return launch_d<64>(a, stream);
     case 96: return launch_d<96>(a, stream);
     case 128: return launch_d<128>(a, stream);
+    case 256: return launch_d<256>(a, stream);
     default: return hipErrorInvalidValue;
   }
 }

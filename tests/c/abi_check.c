@@ -28,8 +28,8 @@ int main(void) {
   expect("fa_fwd scale nan", fa_fwd(p, p, p, p, f, 1, 1, 64, 128, 1, NAN, NULL), FA_ERR_UNSUPPORTED);
   expect("fa_fwd misaligned o", fa_fwd(p, p, p, mis, f, 1, 1, 64, 128, 1, 0.088f, NULL),
          FA_ERR_ALIGN);
-  expect("fa_fwd_fp8 d = 256",
-         fa_fwd_fp8(p, p, p, 1.f, 1.f, 1.f, p, f, 1, 1, 64, 256, 1, 0.0625f, NULL),
+  expect("fa_fwd_fp8 d = 512",
+         fa_fwd_fp8(p, p, p, 1.f, 1.f, 1.f, p, f, 1, 1, 64, 512, 1, 0.0625f, NULL),
          FA_ERR_UNSUPPORTED);
 
   const size_t ws = fa_bwd_workspace_bytes(2, 3, 100, 128);

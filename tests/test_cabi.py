@@ -81,7 +81,7 @@ def test_fwd_rejections(lib):
     assert fwd8(lib, d=32) == UNSUP
     assert fwd(lib, d=32) == UNSUP
     assert fwd(lib, d=512) == UNSUP
-    assert fwd8(lib, d=256) == UNSUP
+    assert fwd8(lib, d=160) == UNSUP
     for bad in (0.0, -0.5, math.inf, math.nan):
         assert fwd(lib, scale=bad) == UNSUP
     assert fwd(lib, v=MIS) == ALIGN
@@ -96,7 +96,7 @@ def fwd8(lib, d=128, qs=1.0, ks=1.0, vs=1.0, k8=P, scale=0.09):
 
 def test_fwd_fp8_rejections(lib):
     assert fwd8(lib, k8=None) == NULL
-    assert fwd8(lib, d=256) == UNSUP                    # fp8 forward: d ∈ {64, 96, 128}
+    assert fwd8(lib, d=512) == UNSUP
     assert fwd8(lib, d=80) == UNSUP
     assert fwd8(lib, qs=0.0) == UNSUP
     assert fwd8(lib, vs=math.nan) == UNSUP

@@ -131,18 +131,18 @@ def test_fp8_bwd_small(N, causal):
     _both(inp, causal, 1.0 / math.sqrt(128), range(2))
 
 
-@pytest.mark.parametrize("d", [64, 96])
+@pytest.mark.parametrize("d", [64, 96, 256])
 @pytest.mark.parametrize("causal", [False, True])
 def test_fp8_fwd_bwd_other_head_dims(d, causal):
-    """The FP8 forward and backward together at d = 64 and 96."""
+    """The FP8 forward and backward together at d = 64, 96 and 256."""
     inp = _case(1, 2, 300, d, seed=5 * d + int(causal))
     _both(inp, causal, 1.0 / math.sqrt(d), range(2))
 
 
 @pytest.mark.parametrize("d", [64, 96, 256])
 def test_fp8_bwd_other_head_dims(d):
-    """The widening and scale folding do not depend on the head dimension, so the backward alone is
-    checked at every head dimension (the fp8 forward has no d = 256)."""
+    """The widening and scale folding do not depend on the head dimension: the backward alone, fed
+    the oracle's O and LSE, at every head dimension."""
     inp = _case(1, 2, 200, d, seed=d)
     scale = 1.0 / math.sqrt(d)
     ref = _oracle_heads(inp, True, scale, range(2))

@@ -571,39 +571,46 @@ def test_fp8_workload_reduced():
     _check_fp8_heads(inp, o, lse, w.causal, w.scale, range(2))
 
 
-@pytest.mark.parametrize("d", [64, 96])
+@pytest.mark.parametrize("d", [64, 96, 256])
 @pytest.mark.parametrize("N", [1, 17, 64, 129, 300, 1000])
 @pytest.mark.parametrize("causal", [False, True])
 def test_fp8_other_head_dims(d, N, causal):
-    """d = 64 (one k-step, 64-byte LDS rows with their own swizzle) and d = 96 (128-byte LDS rows
-    whose last 32 bytes the copy fills with zeros, Q's last 32 columns zero, three V blocks)."""
+    """d = 64 (one k-step, 64-byte LDS rows with their own swizzle), d = 96 (128-byte LDS rows whose
+    last 32 bytes the copy fills with zeros, Q's last 32 columns zero, three V blocks) and d = 256
+    (two workgroups per query tile, one per column half of O; only the first writes LSE)."""
     inp = _fp8_case(1, 2, N, seed=7 * N + d + int(causal), d=d)
     scale = 1.0 / math.sqrt(d)
     o, lse = _run_fp8(inp, causal, scale)
     _check_fp8_heads(inp, o, lse, causal, scale, range(2))
 
 
-@pytest.mark.parametrize("d", [64, 96])
+@pytest.mark.parametrize("d", [64, 96, 256])
 def test_fp8_other_head_dims_row0_exact(d):
-    """Row 0 under the causal mask at d = 64 and 96: O_0 = bf16(V_0) of the dequantised values, so a
-    column lost or taken from the zero padding shows exactly."""
+    """Row 0 under the causal mask at d = 64, 96 and 256: O_0 = bf16(V_0) of the dequantised values,
+    so a column lost, taken from the zero padding or written by the wrong column half shows
+    exactly."""
     inp = _fp8_case(2, 2, 70, seed=98 + d, d=d)
     o, _ = _run_fp8(inp, True, 0.1)
     v0 = workloads.dequantized64(inp["v8"], inp["sv"])[:, :, 0].to(torch.float32)
     assert torch.equal(o[:, :, 0], v0.to(torch.bfloat16))
 
 
-@pytest.mark.parametrize("name", ["fp8_d64_8k", "fp8_d96_8k"])
+@pytest.mark.parametrize("name", ["fp8_d64_8k", "fp8_d96_8k", "fp8_d256_8k"])
 def test_fp8_other_head_dims_workload(name):
-    """fp8_d64_8k and fp8_d96_8k at full size, as the bench runs them: every output finite; four
-    sampled heads in full against the oracle; in every head the first 64 rows and 8 random rows,
-    each computed on its own by the oracle."""
+    """fp8_d64_8k, fp8_d96_8k and fp8_d256_8k at full size, as the bench runs them: every output
+    finite; sampled heads in full against the oracle (two of them at d = 256, four otherwise); in
+    every head the first 64 rows and 8 random rows, each computed on its own by the oracle.  The
+    first rows of a causal head see one to a few keys, where rounding P to e4m3 moves O the most;
+    there, as for the bf16 path's causal rows, the bound is 6e-2 plus half a bf16 ulp of O*, the
+    storage rounding of the output (fp8_d256_8k head 58, row 2: 0.0602, and a CPU emulation of the
+    e4m3 rounding of P and the bf16 rounding of O gives the same value)."""
     w = workloads.WORKLOADS[name]
     inp = workloads.make_inputs(name)
     o, lse = _run_fp8(inp, w.causal, w.scale)
     assert bool(torch.isfinite(o.float()).all()) and bool(torch.isfinite(lse).all())
     B, H, N, d = w.shape()
-    _check_fp8_heads(inp, o, lse, w.causal, w.scale, [0, 37, 90, B * H - 1])
+    heads = [0, B * H - 1] if d == 256 else [0, 37, 90, B * H - 1]
+    _check_fp8_heads(inp, o, lse, w.causal, w.scale, heads)
     q, k, v = (workloads.dequantized64(inp[n + "8"], inp["s" + n]).reshape(B * H, N, d)
                for n in ("q", "k", "v"))
     of = o.reshape(B * H, N, d)
@@ -613,9 +620,9 @@ def test_fp8_other_head_dims_workload(name):
         rows = list(range(64)) + sorted(rnd.randrange(64, N) for _ in range(8))
         o_ref, _ = oracle.attention_rows64(q[h].numpy(), k[h].numpy(), v[h].numpy(), rows, True,
                                            w.scale)
-        e = float(np.abs(_np64(of[h][rows]) - o_ref).max())
-        assert e <= FP8_O_TOL, (h, e)
-        worst = max(worst, e)
+        err = np.abs(_np64(of[h][rows]) - o_ref)
+        assert np.all(err <= FP8_O_TOL + _half_ulp_bf16(o_ref)), (h, float(err.max()))
+        worst = max(worst, float(err.max()))
     print(f"{name} rows check: worst |O - O*| = {worst:.4g} over {B * H} heads")
 
 

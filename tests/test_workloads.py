@@ -8,11 +8,12 @@ import workloads
 
 def test_workload_table():
     w = workloads.WORKLOADS
-    assert [x.number for x in w.values()] == [1, 2, 3, 4, 5, 8, 9, 10, 11, 12]
+    assert [x.number for x in w.values()] == [1, 2, 3, 4, 5, 8, 9, 10, 11, 12, 13]
     assert w["fp8bwd_8k"].fp8 and w["fp8bwd_8k"].backward
     assert w["d96_4k"].shape() == (4, 32, 4096, 96)
     assert w["d256_4k"].shape() == (4, 16, 4096, 256) and w["d256_4k"].causal
     assert w["d256_4k"].fwd_flops() == w["causal_4k"].fwd_flops()
+    assert w["fp8_d256_8k"].fwd_flops() == w["fp8_8k"].fwd_flops() and w["fp8_d256_8k"].fp8
     assert w["causal_4k"].shape() == (4, 32, 4096, 128) and w["causal_4k"].causal
     # forward 4·B·H·N²·d halved when causal; backward 2.5× forward
     assert w["causal_4k"].fwd_flops() == 4 * 4 * 32 * 4096 ** 2 * 128 / 2
