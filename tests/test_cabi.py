@@ -229,6 +229,10 @@ def test_decode_rejections(lib):
     assert decode(lib, Nq=9, Nk=8) == SHAPE
     assert decode(lib, B=0) == SHAPE
     assert decode(lib, Nk=1 << 23, d=128) == SHAPE  # per-head cache past 32-bit offsets
+    # the exact limit, (Nk + 256) · d · 2 < 2^31: one key more is refused, the largest cache passes
+    # the shape checks (and stops at the missing workspace, before any HIP call)
+    assert decode(lib, Nk=(1 << 23) - 256, d=128) == SHAPE
+    assert decode(lib, Nk=(1 << 23) - 257, d=128, ws=None) == WORKSPACE
     assert decode(lib, d=80) == UNSUP
     assert decode(lib, scale=0.0) == UNSUP
     assert decode(lib, scale=math.inf) == UNSUP

@@ -165,3 +165,19 @@ def test_decode_other_softmax_scales(scale):
     v = torch.randn(1, 2, 1500, 128, generator=g).to(torch.bfloat16)
     o, lse = _run(q, k, v, True, scale)
     _check(q, k, v, o, lse, True, scale, o_tol="bf16_store")
+
+
+def test_decode_largest_head():
+    """The largest cache one head may hold at d = 128: the kernels address a head with 32-bit byte
+    offsets and the library accepts (Nk + 256) · d · 2 < 2^31, so Nk = 2^23 − 257 keys (2 GiB each for
+    K and V, a ragged last tile and chunk).  Four queries, causal, checked against the oracle."""
+    Nq, Nk, d = 4, (1 << 23) - 257, 128
+    scale = 1.0 / math.sqrt(d)
+    g = torch.Generator(device="cuda").manual_seed(23)
+    q = torch.randn(1, 1, Nq, d, device="cuda", generator=g).to(torch.bfloat16)
+    k = torch.randn(1, 1, Nk, d, device="cuda", generator=g).to(torch.bfloat16)
+    v = torch.randn(1, 1, Nk, d, device="cuda", generator=g).to(torch.bfloat16)
+    o, lse = fa().decode(q, k, v, True, scale)
+    torch.cuda.synchronize()
+    worst = _check(q.cpu(), k.cpu(), v.cpu(), o, lse, True, scale)
+    print(f"Nk = {Nk}: worst |O - O*| = {worst[0]:.3g}, |LSE - LSE*| = {worst[1]:.3g}")
