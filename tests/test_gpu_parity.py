@@ -475,6 +475,49 @@ def test_million_keys_one_head():
     _check_bwd_sums(do, dk, dv)
 
 
+def test_more_than_2_32_elements_per_tensor():
+    """Tensors of more than 2^32 elements (10 GiB of bf16 each): 262146 causal heads of 160 keys at
+    d = 128, so head offsets pass 2^31 and 2^32 elements.  Sampled heads at the start, at those two
+    boundaries and at the end against the oracle; on every head, the exact first causal row (O_0 = V_0
+    bitwise, LSE_0 = scale · q_0 · k_0) and the sums Σ_j dV_j = Σ_i dO_i and Σ_j dK_j = 0."""
+    B, H, N, d = 2, 131073, 160, 128
+    BH = B * H
+    assert BH * N * d > 1 << 32
+    scale = 1.0 / math.sqrt(d)
+    dev = torch.device("cuda")
+    g = torch.Generator(device=dev).manual_seed(32)
+    q, k, v, do = (torch.randn(B, H, N, d, device=dev, dtype=torch.bfloat16, generator=g)
+                   for _ in range(4))
+    o, lse = fa().fwd(q, k, v, True, scale)
+    dq, dk, dv = fa().bwd(q, k, v, o, lse, do, True, scale)
+    torch.cuda.synchronize()
+
+    assert torch.equal(o[:, :, 0], v[:, :, 0])
+    l0 = (q[:, :, 0].float() * k[:, :, 0].float()).sum(-1) * scale
+    assert (lse[:, :, 0] - l0).abs().max().item() <= 1e-3
+    worst_v = worst_k = 0.0
+    for h0 in range(0, BH, 16384):  # the sums over every head, a slice of heads at a time
+        sl = slice(h0, min(BH, h0 + 16384))
+        sdv = dv.view(BH, N, d)[sl].double().sum(1)
+        sdo = do.view(BH, N, d)[sl].double().sum(1)
+        worst_v = max(worst_v, ((sdv - sdo).norm(dim=-1) / sdo.norm(dim=-1).clamp_min(1e-6)).max().item())
+        dks = dk.view(BH, N, d)[sl].double()
+        worst_k = max(worst_k, (dks.sum(1).norm(dim=-1) / dks.norm(dim=(1, 2)).clamp_min(1e-12)).max().item())
+    assert worst_v <= GRAD_TOL and worst_k <= GRAD_TOL, (worst_v, worst_k)
+
+    per_head = N * d
+    heads = [0, (1 << 31) // per_head, (1 << 31) // per_head + 1, (1 << 32) // per_head, BH - 1]
+
+    def sample(t):
+        return t.reshape(BH, *t.shape[2:])[heads].cpu().unsqueeze(0)
+
+    qs, ks, vs, dos, os_, ls, dqs, dks_, dvs = (sample(t) for t in (q, k, v, do, o, lse, dq, dk, dv))
+    _check_fwd_heads(qs, ks, vs, os_, ls, True, scale, o_tol="bf16_store")
+    _check_bwd_heads(qs, ks, vs, dos, dqs, dks_, dvs, True, scale, range(len(heads)))
+    del q, k, v, do, o, lse, dq, dk, dv
+    torch.cuda.empty_cache()  # hand the ~86 GB back before the tests that follow
+
+
 @pytest.mark.parametrize("d", [96, 128, 256])
 def test_bwd_phases_equal_fused_call(d):
     """fa_bwd_preprocess + fa_bwd_dkdv + fa_bwd_dq give bitwise what fa_bwd gives, and fa_bwd is
