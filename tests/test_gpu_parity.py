@@ -508,6 +508,32 @@ def test_million_keys_one_head():
     _check_bwd_sums(do, dk, dv)
 
 
+def test_fwd_largest_head():
+    """The forward on the largest head the library accepts at d = 128: (N + 256) · d · 2 < 2^31, so
+    N = 2^23 − 257 causal keys (2 GiB per tensor, ragged last tile; ≈ 1.8·10^16 FLOP).  Blocks of rows
+    at the start, the middle and the end against the oracle's row-restricted form, and the exact
+    first row."""
+    B, H, N, d = 1, 1, (1 << 23) - 257, 128
+    scale = 1.0 / math.sqrt(d)
+    g = torch.Generator(device="cuda").manual_seed(31)
+    q, k, v = (torch.randn(B, H, N, d, device="cuda", dtype=torch.bfloat16, generator=g)
+               for _ in range(3))
+    o, lse = fa().fwd(q, k, v, True, scale)
+    torch.cuda.synchronize()
+    assert torch.equal(o[0, 0, 0], v[0, 0, 0])
+    assert bool(torch.isfinite(o).all()) and bool(torch.isfinite(lse).all())
+    q64, k64, v64 = (x[0, 0].cpu().double().numpy() for x in (q, k, v))
+    o_c, l_c = o[0, 0].cpu(), lse[0, 0].cpu()
+    for r0 in (0, N // 2 - 3, N - 5):
+        o_ref, l_ref = oracle.attention_head_fwd64(q64[r0:r0 + 5], k64[:r0 + 5], v64[:r0 + 5], True,
+                                                  scale, q_offset=r0)
+        err = np.abs(_np64(o_c[r0:r0 + 5]) - o_ref)
+        assert np.all(err <= O_TOL + _half_ulp_bf16(o_ref)), (r0, float(err.max()))
+        assert np.abs(_np64(l_c[r0:r0 + 5]) - l_ref).max() <= LSE_TOL, r0
+    del q, k, v, o, lse
+    torch.cuda.empty_cache()
+
+
 def test_more_than_2_32_elements_per_tensor():
     """Tensors of more than 2^32 elements (10 GiB of bf16 each): 262146 causal heads of 160 keys at
     d = 128, so head offsets pass 2^31 and 2^32 elements.  Sampled heads at the start, at those two
