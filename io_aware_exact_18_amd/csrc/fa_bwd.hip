@@ -428,7 +428,7 @@ template <int D, bool CAUSAL, int OUT>
 hipError_t launch_dkdv_pass(const BwdArgs& a, hipStream_t stream) {
   const int nkt = (a.N + kBKV - 1) / kBKV;
   const uint32_t total = (uint32_t)a.B * a.H * nkt;
-  const int remap = (total % 8u == 0u) ? 1 : 0;
+  const int remap = use_xcd_order(total, (long)a.B * a.H, CAUSAL ? 1 : 0);
   hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, OUT>), dim3(total), dim3(kThreads), 0, stream,
                      (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, a.lse,
                      (const bf16*)a.dout, (const float*)a.delta, (bf16*)a.dk, (bf16*)a.dv, a.N, nkt,
@@ -451,7 +451,7 @@ template <int D, bool CAUSAL>
 hipError_t launch_dq(const BwdArgs& a, hipStream_t stream) {
   const int nqt = (a.N + kBR - 1) / kBR;
   const uint32_t total = (uint32_t)a.B * a.H * nqt;
-  const int remap = (total % 8u == 0u) ? 1 : 0;
+  const int remap = use_xcd_order(total, (long)a.B * a.H, CAUSAL ? 1 : 0);
   hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3(total), dim3(kThreads), 0, stream,
                      (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, a.lse,
                      (const bf16*)a.dout, (const float*)a.delta, (bf16*)a.dq, a.N, nqt, a.dq_scale,

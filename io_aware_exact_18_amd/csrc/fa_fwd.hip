@@ -457,7 +457,7 @@ template <bool CAUSAL>
 hipError_t launch_split(const FwdArgs& a, hipStream_t stream) {
   const int nqt = (a.N + kBR - 1) / kBR;
   const uint32_t total = (uint32_t)a.B * a.H * nqt;
-  const int remap = (total % 8u == 0u) ? 1 : 0;
+  const int remap = use_xcd_order(total, (long)a.B * a.H, CAUSAL ? 1 : 0);
   hipLaunchKernelGGL((fwd_bf16_split_kernel<256, CAUSAL>), dim3(total), dim3(kSplitThreads), 0,
                      stream, (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, (bf16*)a.o, a.lse,
                      a.N, nqt, a.scale * kLog2e, remap);
@@ -468,7 +468,7 @@ template <int D, bool CAUSAL>
 hipError_t launch(const FwdArgs& a, hipStream_t stream) {
   const int nqt = (a.N + kBR - 1) / kBR;
   const uint32_t total = (uint32_t)a.B * a.H * nqt;
-  const int remap = (total % 8u == 0u) ? 1 : 0;
+  const int remap = use_xcd_order(total, (long)a.B * a.H, CAUSAL ? 1 : 0);
   const float scale_log2 = a.scale * kLog2e;
   hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL>), dim3(total), dim3(kThreads), 0, stream,
                      (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, (bf16*)a.o, a.lse, a.N,

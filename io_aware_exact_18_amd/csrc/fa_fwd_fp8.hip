@@ -307,7 +307,7 @@ template <int D, bool CAUSAL>
 hipError_t launch(const Fp8FwdArgs& a, hipStream_t stream) {
   const int nqt = (a.N + kBR - 1) / kBR;
   const uint32_t total = (uint32_t)a.B * a.H * nqt * col_splits<D>();
-  const int remap = (total % 8u == 0u) ? 1 : 0;
+  const int remap = use_xcd_order(total, (long)a.B * a.H, CAUSAL ? 1 : 0);
   const float c_log2 = a.scale * a.q_descale * a.k_descale * kLog2e;
   hipLaunchKernelGGL((fwd_fp8_kernel<D, CAUSAL>), dim3(total), dim3(kThreads), 0, stream,
                      (const uint8_t*)a.q8, (const uint8_t*)a.k8, (const uint8_t*)a.v8, (bf16*)a.o,
