@@ -71,5 +71,22 @@ def build(verbose=False, extra_flags=()):
     return LIB_PATH
 
 
+PROBE_SRC = os.path.join(ROOT, "tests", "hip", "fa_probe.hip")
+PROBE_LIB = os.path.join(ROOT, "tests", "hip", "libfa_probe.so")
+
+
+def build_probe():
+    """Compile the tests' conversion probe (tests/hip/fa_probe.hip, not part of libfa.so) into
+    tests/hip/libfa_probe.so with the library's flags; returns its path."""
+    tmp = PROBE_LIB + ".tmp"
+    cmd = [hipcc(), *COMMON_FLAGS, "-shared", PROBE_SRC, "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for the probe:\n{' '.join(cmd)}\n{r.stderr[-4000:]}")
+    os.replace(tmp, PROBE_LIB)
+    return PROBE_LIB
+
+
 if __name__ == "__main__":
     print(build(verbose="-v" in sys.argv))
+    print(build_probe())

@@ -170,9 +170,27 @@ fa_status fa_bwd_dq(const void* q, const void* k, const void* v, const float* ls
   return fa::launch_bwd_dq(a, stream) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
+}  // extern "C"
+
+namespace {
+
+// Shape checks of a decode call (everything fa_decode rejects before looking at pointers, scale
+// and workspace).
+fa_status check_decode_shape(int B, int H, int Nq, int Nk, int d) {
+  if (B < 1 || H < 1 || Nq < 1 || Nq > 32 || Nk < Nq) return FA_ERR_SHAPE;
+  fa_status st = check_shape(B, H, Nk, d, 2);  // the cache: per-head offsets, totals, grid
+  if (st != FA_OK) return st;
+  const fa::DecodeSplit sp = fa::decode_split(B, H, Nq, Nk);
+  if ((uint64_t)B * (uint64_t)H * (uint64_t)sp.S >= (1ull << 31)) return FA_ERR_SHAPE;
+  return FA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
 size_t fa_decode_workspace_bytes(int B, int H, int Nq, int Nk, int d) {
-  if (B < 1 || H < 1 || Nq < 1 || Nq > 32 || Nk < Nq) return 0;
-  if (d != 64 && d != 96 && d != 128 && d != 256) return 0;
+  if (check_decode_shape(B, H, Nq, Nk, d) != FA_OK) return 0;
   return fa::decode_workspace_bytes(B, H, Nq, Nk, d);
 }
 
@@ -180,11 +198,8 @@ fa_status fa_decode(const void* q, const void* k, const void* v, void* o, float*
                     void* workspace, size_t workspace_bytes, int B, int H, int Nq, int Nk, int d,
                     int causal, float softmax_scale, hipStream_t stream) {
   if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
-  if (B < 1 || H < 1 || Nq < 1 || Nq > 32 || Nk < Nq) return FA_ERR_SHAPE;
-  fa_status st = check_shape(B, H, Nk, d, 2);  // the cache: per-head offsets, totals, grid
+  fa_status st = check_decode_shape(B, H, Nq, Nk, d);
   if (st != FA_OK) return st;
-  const fa::DecodeSplit sp = fa::decode_split(B, H, Nq, Nk);
-  if ((uint64_t)B * (uint64_t)H * (uint64_t)sp.S >= (1ull << 31)) return FA_ERR_SHAPE;
   if (!good_scale(softmax_scale)) return FA_ERR_UNSUPPORTED;
   if (!workspace || workspace_bytes < fa::decode_workspace_bytes(B, H, Nq, Nk, d))
     return FA_ERR_WORKSPACE;

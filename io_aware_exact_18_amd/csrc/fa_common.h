@@ -98,6 +98,14 @@ __device__ inline uint32_t pack_bf16x2(float lo, float hi) {
 
 __device__ inline float bf16_bits_to_float(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
 
+// Four fp32 values → four OCP e4m3fn bytes (round to nearest even), first in the lowest byte.  The
+// conversion does not saturate: a magnitude above 464 (the midpoint between 448 and 480) gives the
+// NaN code.  Callers keep their values within ±448.
+__device__ inline uint32_t pack_e4m3x4(float p0, float p1, float p2, float p3) {
+  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, 0, false);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, lo, true);
+}
+
 // LDS tile layout for a [rows][D] bf16 tile with no padding: the 16-byte chunk c of row r is stored at
 // chunk c ^ H(r).  gfx950's LDS has 64 four-byte banks and serves 16 lanes of a 16-byte read (32 lanes
 // of an 8-byte read) per pass; H is chosen so both access patterns the kernels use are conflict-free:

@@ -8,8 +8,9 @@
 //
 //   * Sᵀ = K Qᵀ on v_mfma_f32_32x32x64_f8f6f4 (fp32 accumulation; products of e4m3 values are exact).
 //     The descales and scale·log2(e) fold into the one FMA that forms the exponent.
-//   * P = 2^(s − m + 6) ∈ [0, 256] is rounded to e4m3 (v_cvt_pk_fp8_f32: round-to-nearest-even,
-//     saturating at 448) and Oᵀ += Vᵀ Pᵀ runs on the same fp8 matrix core.  m is a reference maximum
+//   * P = 2^(s − m + 6) ∈ [0, 256] is rounded to e4m3 (v_cvt_pk_fp8_f32: round-to-nearest-even;
+//     it does not saturate, but P stays far below 448) and Oᵀ += Vᵀ Pᵀ runs on the same fp8 matrix
+//     core.  m is a reference maximum
 //     that trails the running maximum by at most 2, so P ≤ 2^8; the factor 2^6 (free: it is part of
 //     the FMA's constant) keeps small probabilities out of e4m3's subnormal range; both cancel in
 //     O = Σ P V / Σ P and are removed from LSE.  The row sum l is formed by one more
@@ -78,12 +79,6 @@ __device__ inline u32x2 lds_read_tr8(const uint8_t* p) {
   typedef int i32x2_t __attribute__((ext_vector_type(2)));
   i32x2_t r = __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) i32x2_t*)(p));
   return __builtin_bit_cast(u32x2, r);
-}
-
-// Four fp32 values → four e4m3 bytes (round to nearest even, saturating), first in the lowest byte.
-__device__ inline uint32_t pack_e4m3x4(float p0, float p1, float p2, float p3) {
-  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, 0, false);
-  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, lo, true);
 }
 
 template <int D, bool CAUSAL>

@@ -211,9 +211,12 @@ def test_decode_workspace_formula(lib):
         assert (S - 1) * length < Nk <= S * length
         want = -(-(B * H * S * Nq * (d + 2) * 4) // 256) * 256
         assert lib.fa_decode_workspace_bytes(B, H, Nq, Nk, d) == want, (B, H, Nq, Nk, d)
+    # Every shape fa_decode rejects gets 0, including a cache past the 32-bit per-head offsets.
     for bad in ((0, 1, 1, 8, 64), (1, 1, 0, 8, 64), (1, 1, 33, 64, 64), (1, 1, 9, 8, 64),
-                (1, 1, 1, 8, 80), (1, 1, 1, 8, 512)):
+                (1, 1, 1, 8, 80), (1, 1, 1, 8, 512), (1, 1, 1, 1 << 23, 128),
+                (1, 1, 1, (1 << 23) - 256, 128)):
         assert lib.fa_decode_workspace_bytes(*bad) == 0, bad
+    assert lib.fa_decode_workspace_bytes(1, 1, 1, (1 << 23) - 257, 128) > 0
 
 
 def decode(lib, q=P, k=P, v=P, o=P, lse=P, ws=P, ws_bytes=1 << 30, B=1, H=1, Nq=1, Nk=64, d=64,
@@ -253,3 +256,4 @@ def test_binding_rejects_mixed_devices_without_a_gpu():
                                                                  True)):
         with pytest.raises(ValueError):
             call()
+

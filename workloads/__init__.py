@@ -181,16 +181,21 @@ def enlarge_keys(k, seed, block=1024, factor=8.0):
     return out
 
 
+def round_e4m3(x):
+    """float32 → e4m3fn codes: e4m3(RNE(clamp(x, ±448))), saturating at the largest finite value.
+    The clamp keeps torch's cast from turning values just past 448 into NaN."""
+    return x.clamp(-E4M3_MAX, E4M3_MAX).to(torch.float8_e4m3fn)
+
+
 def quantize_e4m3(x):
     """Per-tensor e4m3fn quantisation: s = amax|x| / 448 (fp32), x8 = e4m3(RNE(clamp(x / s, ±448))).
 
-    Returns (x8 as torch.float8_e4m3fn, s as a Python float).  The clamp keeps torch's cast from turning
-    values just past 448 into NaN.
+    Returns (x8 as torch.float8_e4m3fn, s as a Python float).
     """
     amax = float(x.abs().max())
     s = amax / E4M3_MAX if amax > 0 else 1.0
     s = float(torch.tensor(s, dtype=torch.float32))
-    x8 = (x / s).clamp(-E4M3_MAX, E4M3_MAX).to(torch.float8_e4m3fn)
+    x8 = round_e4m3(x / s)
     return x8, s
 
 
