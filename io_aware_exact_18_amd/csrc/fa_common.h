@@ -98,6 +98,18 @@ __device__ inline uint32_t pack_bf16x2(float lo, float hi) {
 
 __device__ inline float bf16_bits_to_float(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
 
+// acc + the sum of the eight bf16 values of v, in fp32 (four v_dot2c_f32_bf16 against (1, 1)).
+__device__ inline float sum_bf16x8(bf16x8 v, float acc) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const bf16x2_t one = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const bf16x2_t pair = {v[2 * i], v[2 * i + 1]};
+    acc = __builtin_amdgcn_fdot2_f32_bf16(pair, one, acc, false);
+  }
+  return acc;
+}
+
 // Four fp32 values → four OCP e4m3fn bytes (round to nearest even), first in the lowest byte.  The
 // conversion does not saturate: a magnitude above 464 (the midpoint between 448 and 480) gives the
 // NaN code.  Callers keep their values within ±448.

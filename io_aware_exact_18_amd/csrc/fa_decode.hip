@@ -15,7 +15,9 @@
 //     32×32×16 bf16 matrix core with the queries as the 32 columns (rows past Nq are zero and
 //     discarded), runs the online softmax of "Anatomy of a FlashAttention Kernel", section "What is
 //     online softmax and how does tiling keep it exact?", and writes the chunk's unnormalised output
-//     with its row maximum and row sum (fp32) to the workspace.
+//     with its row maximum and two row sums (fp32) to the workspace: over the fp32 probabilities (for
+//     LSE) and over the same values rounded to bf16, the weights P·V applies (O is divided by it, as
+//     in the forward kernel).
 //   * decode_merge_kernel: per (batch·head, query) combines the chunks by their softmax mass — the same
 //     recurrence applied to whole chunks — and writes O (bf16) and LSE (fp32, natural log).
 // Chunks of one head are consecutive workgroups and so run on different XCDs (round-robin dispatch);
@@ -77,6 +79,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
 
   float m = -INFINITY;  // reference maximum of the base-2 scaled scores (raised past kDecSlack)
   float l = 0.f;        // Σ 2^(t − m) over this lane's half of the keys
+  float lr = 0.f;       // the same over the bf16-rounded values that enter P·V
   f32x16 oacc[DB];      // Oᵀ: rows d = 32b + 8(r/4) + 4g + r%4, column = this lane's query
 #pragma unroll
   for (int b = 0; b < DB; ++b)
@@ -117,6 +120,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
       const float m_new = fmaxf(m, mt);
       const float alpha = exp2_fast(m - (m_new == -INFINITY ? 0.f : m_new));
       l *= alpha;
+      lr *= alpha;
 #pragma unroll
       for (int b = 0; b < DB; ++b)
 #pragma unroll
@@ -135,6 +139,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
       pf[r >> 3][r & 7] = (__bf16)p;
     }
     l += (rs[0] + rs[1]) + (rs[2] + rs[3]);
+    lr = sum_bf16x8(pf[1], sum_bf16x8(pf[0], lr));
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       bf16x8 vf[DB];
@@ -152,8 +157,9 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
   wait_vmem_all();
 
   // The chunk's result for this lane's query: unnormalised Oᵀ column, reference maximum m (base 2)
-  // and row sum l.  Layout: part_o [BH][S][Nq][D], part_ml [BH][S][Nq][2].
+  // and the row sums l and lr.  Layout: part_o [BH][S][Nq][D], part_ml [BH][S][Nq][3].
   const float l_tot = halves_sum(l);
+  const float lr_tot = halves_sum(lr);
   if (lc < Nq) {
     const size_t row = ((size_t)bh * S + sp) * Nq + lc;
     float* orow = part_o + row * D;
@@ -166,8 +172,9 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
         *(f32x4*)&orow[32 * b + 8 * r4 + 4 * g] = w;
       }
     if (g == 0) {
-      part_ml[2 * row] = m;
-      part_ml[2 * row + 1] = l_tot;
+      part_ml[3 * row] = m;
+      part_ml[3 * row + 1] = l_tot;
+      part_ml[3 * row + 2] = lr_tot;
     }
   }
 }
@@ -185,20 +192,21 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(const float* __restric
   const int qi = blockIdx.x % Nq;
   const size_t row0 = (size_t)bh * S * Nq + qi;  // chunk s: row0 + s·Nq
   float m = -INFINITY;
-  for (int s = 0; s < S; ++s) m = fmaxf(m, part_ml[2 * (row0 + (size_t)s * Nq)]);
-  float l = 0.f, acc[PER];
+  for (int s = 0; s < S; ++s) m = fmaxf(m, part_ml[3 * (row0 + (size_t)s * Nq)]);
+  float l = 0.f, lr = 0.f, acc[PER];
 #pragma unroll
   for (int t = 0; t < PER; ++t) acc[t] = 0.f;
   for (int s = 0; s < S; ++s) {
     const size_t row = row0 + (size_t)s * Nq;
-    const float ms = part_ml[2 * row];
+    const float ms = part_ml[3 * row];
     const float w = exp2_fast(ms - m);  // 0 for a chunk without usable keys (ms = -inf)
-    l += w * part_ml[2 * row + 1];
+    l += w * part_ml[3 * row + 1];
+    lr += w * part_ml[3 * row + 2];
 #pragma unroll
     for (int t = 0; t < PER; ++t)
       if (D % 64 == 0 || lane + 64 * t < D) acc[t] += w * part_o[row * D + lane + 64 * t];
   }
-  const float inv = 1.f / l;
+  const float inv = 1.f / lr;
   const size_t orow = ((size_t)bh * Nq + qi) * D;
 #pragma unroll
   for (int t = 0; t < PER; ++t)

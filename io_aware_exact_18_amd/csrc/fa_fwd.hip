@@ -26,6 +26,11 @@
 //   * The softmax runs in base 2 with scale·log2(e) folded into one FMA; normalisation by the row sum
 //     is deferred to the end (fewer non-matmul operations, same section).  LSE is converted back to
 //     natural log on output.
+//   * Two row sums are kept: l over the fp32 probabilities, for LSE, and lr over the same values
+//     rounded to bf16 — the weights the P·V product actually applies — which O is divided by.  O is
+//     then an exactly normalised average of V rows under the rounded weights: in a row dominated by
+//     one key it returns that key's V row however p rounds, where dividing by l would leave p's
+//     rounding error (up to 2^-9 of |V|) in O.
 //   * Grid: one workgroup per (batch·head, query tile); query tiles of one head are kept on one XCD so
 //     the head's K/V stay in that XCD's L2; under the causal mask the heaviest tiles start first.
 //   * Head dimension 256 runs fwd_bf16_split_kernel instead: 8 waves per workgroup, each key tile
@@ -148,6 +153,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
 
   float m = -INFINITY;  // reference maximum of the base-2 scaled scores (see kSlack)
   float l = 0.f;        // running sum of 2^(t - m) over this lane's keys (half of the row)
+  float lr = 0.f;       // the same sum over the bf16-rounded values that enter P·V
   f32x16 oacc[DB];
 #pragma unroll
   for (int b = 0; b < DB; ++b)
@@ -187,6 +193,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
         const float m_new = fmaxf(m, mt);
         const float alpha = exp2_fast(m - (m_new == -INFINITY ? 0.f : m_new));
         l *= alpha;
+        lr *= alpha;
 #pragma unroll
         for (int b = 0; b < DB; ++b)
 #pragma unroll
@@ -237,6 +244,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
 #pragma unroll
         for (int r = (kb == 0 ? 4 : 0); r < 16; ++r) rs[r & 3] += s_cur[kb][r];
       l += (rs[0] + rs[1]) + (rs[2] + rs[3]);
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) lr = sum_bf16x8(pf[ks], lr);
       mx = rowmax(s_nxt);
 #pragma unroll
       for (int i = 0; i < 2 * KSTEPS; ++i) {
@@ -253,9 +262,9 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     if (j + 1 < ntiles) tile(std::integral_constant<int, 1>{}, j + 1);
   }
 
-  // Epilogue: combine the two half-row sums, normalise, write O and LSE.
+  // Epilogue: combine the two half-row sums, normalise by the rounded weights' sum, write O and LSE.
   const float l_tot = halves_sum(l);
-  const float inv = 1.f / l_tot;
+  const float inv = 1.f / halves_sum(lr);
   if (qi < N) {
     bf16* orow = O + head + (size_t)qi * D;
 #pragma unroll
@@ -296,7 +305,7 @@ __global__ __launch_bounds__(kSplitThreads, 1) void fwd_bf16_split_kernel(
   __shared__ __attribute__((aligned(1024))) bf16 k1s[kBC * L];
   __shared__ __attribute__((aligned(1024))) bf16 v0s[kBC * L];
   __shared__ __attribute__((aligned(1024))) bf16 v1s[kBC * L];
-  __shared__ __attribute__((aligned(256))) float xml[4][2][64];  // key half 1: (m, l) per lane
+  __shared__ __attribute__((aligned(256))) float xml[4][3][64];  // key half 1: (m, l, lr) per lane
   static_assert(DB * 16 * 64 * 4 == kBC * L * 2, "one wave's Oᵀ fills one staging buffer");
 
   const int tid = threadIdx.x;
@@ -339,6 +348,7 @@ __global__ __launch_bounds__(kSplitThreads, 1) void fwd_bf16_split_kernel(
 
   float m = -INFINITY;  // reference maximum of the base-2 scaled scores (slack rule as above)
   float l = 0.f;        // partial row sum over this lane's keys of this key half
+  float lr = 0.f;       // the same over the bf16-rounded values that enter P·V (O is divided by it)
   f32x16 oacc[DB];
 #pragma unroll
   for (int b = 0; b < DB; ++b)
@@ -376,6 +386,7 @@ __global__ __launch_bounds__(kSplitThreads, 1) void fwd_bf16_split_kernel(
         const float m_new = fmaxf(m, mt);
         const float alpha = exp2_fast(m - (m_new == -INFINITY ? 0.f : m_new));
         l *= alpha;
+        lr *= alpha;
 #pragma unroll
         for (int b = 0; b < DB; ++b)
 #pragma unroll
@@ -396,6 +407,7 @@ __global__ __launch_bounds__(kSplitThreads, 1) void fwd_bf16_split_kernel(
           pf[ks][e] = (__bf16)p;
         }
       l += (rs[0] + rs[1]) + (rs[2] + rs[3]);
+      lr = sum_bf16x8(pf[1], sum_bf16x8(pf[0], lr));
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
@@ -420,18 +432,20 @@ __global__ __launch_bounds__(kSplitThreads, 1) void fwd_bf16_split_kernel(
       for (int r = 0; r < 16; ++r) xo[(b * 16 + r) * 64 + lane] = oacc[b][r];
     xml[qblk][0][lane] = m;
     xml[qblk][1][lane] = l;
+    xml[qblk][2][lane] = lr;
   }
   __syncthreads();
   if (kh == 0) {
     const float m1 = xml[qblk][0][lane];
     const float l1 = xml[qblk][1][lane];
+    const float lr1 = xml[qblk][2][lane];
     // Key half 0 always holds key 0 of the row (causal) or a full block, so m is finite here for
     // every row with an unmasked key; half 1 may have seen none (m1 = −inf, l1 = 0).
     const float mm = fmaxf(m, m1);
     const float a0 = exp2_fast(m - mm);
     const float a1 = (m1 == -INFINITY) ? 0.f : exp2_fast(m1 - mm);
     const float l_tot = halves_sum(a0 * l + a1 * l1);
-    const float inv = 1.f / l_tot;
+    const float inv = 1.f / halves_sum(a0 * lr + a1 * lr1);
     const float w0 = a0 * inv, w1 = a1 * inv;
     if (qi < N) {
       bf16* orow = O + head + (size_t)qi * D;

@@ -92,10 +92,10 @@ inline DecodeSplit decode_split(int B, int H, int Nq, int Nk) {
   return r;
 }
 // Workspace of a decode call: per (batch·head, chunk, query) the unnormalised output (d fp32) and the
-// chunk's row maximum and row sum (2 fp32), rounded up to 256 bytes.
+// chunk's row maximum and two row sums (3 fp32), rounded up to 256 bytes.
 inline size_t decode_workspace_bytes(int B, int H, int Nq, int Nk, int d) {
   const DecodeSplit sp = decode_split(B, H, Nq, Nk);
-  return (((size_t)B * H * sp.S * Nq * ((size_t)d + 2) * sizeof(float)) + 255u) & ~(size_t)255u;
+  return (((size_t)B * H * sp.S * Nq * ((size_t)d + 3) * sizeof(float)) + 255u) & ~(size_t)255u;
 }
 
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream);

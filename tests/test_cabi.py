@@ -209,7 +209,7 @@ def test_decode_workspace_formula(lib):
                             (1, 2, 5, 999, 96), (2, 2, 4, 4096, 256)):
         S, length = _decode_split(B, H, Nk)
         assert (S - 1) * length < Nk <= S * length
-        want = -(-(B * H * S * Nq * (d + 2) * 4) // 256) * 256
+        want = -(-(B * H * S * Nq * (d + 3) * 4) // 256) * 256
         assert lib.fa_decode_workspace_bytes(B, H, Nq, Nk, d) == want, (B, H, Nq, Nk, d)
     # Every shape fa_decode rejects gets 0, including a cache past the 32-bit per-head offsets.
     for bad in ((0, 1, 1, 8, 64), (1, 1, 0, 8, 64), (1, 1, 33, 64, 64), (1, 1, 9, 8, 64),
