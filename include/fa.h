@@ -21,7 +21,8 @@
  *  Supported  d ∈ {64, 96, 128, 256}; N ≥ 1; B, H ≥ 1; B·H·N·d < 2^40.  bf16 values are IEEE
  *             bfloat16.
  *  Memory     Every pointer is a device pointer owned by the caller and 16-byte aligned.  The library
- *             never allocates or frees device memory and keeps no state between calls.
+ *             never allocates or frees device memory and keeps no state between calls, except for the
+ *             fixed device array behind fa_bwd_noalloc (see there).
  *  Streams    Every call only enqueues work on `stream` and returns; results are ready when the stream
  *             reaches that point.  Calls are re-entrant and may be made on several streams at once.
  *  Errors     Arguments are checked before any HIP call; a failed check returns its status and enqueues
@@ -162,6 +163,22 @@ size_t fa_decode_workspace_bytes(int B, int H, int Nq, int Nk, int d);
 fa_status fa_decode(const void* q, const void* k, const void* v, void* o, float* lse,
                     void* workspace, size_t workspace_bytes, int B, int H, int Nq, int Nk, int d,
                     int causal, float softmax_scale, hipStream_t stream);
+
+/*
+ * fa_bwd without a workspace argument, for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation).  The D array lives in a
+ * fixed 16 MiB device array inside the library (one copy per device, held until the process ends), so
+ * the call allocates nothing.  Arguments and results as for fa_bwd, plus one limit: B·H·N ≤
+ * fa_bwd_noalloc_max_rows() (= 2^22); larger shapes return FA_ERR_WORKSPACE before any HIP call.
+ * Every call on one device shares that device's array: calls that overlap in time on one device
+ * (several streams or host threads) race and must be serialised by the caller.  The array needs no
+ * initialisation: each call writes every row of D it reads.
+ */
+size_t fa_bwd_noalloc_max_rows(void);
+fa_status fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
+                         const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                         int B, int H, int N, int d, int causal, float softmax_scale,
+                         hipStream_t stream);
 
 /* A static, human-readable name for a status code (never NULL). */
 const char* fa_status_str(fa_status status);

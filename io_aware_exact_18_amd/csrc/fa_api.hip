@@ -4,6 +4,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "../../include/fa.h"
 #include "fa_launch.h"
 
@@ -288,6 +290,90 @@ fa_status fa_bwd_fp8(const void* q8, const void* k8, const void* v8, float q_des
       fa::launch_e4m3_to_bf16(k8, kc, n, stream) != hipSuccess ||
       fa::launch_e4m3_to_bf16(v8, vc, n, stream) != hipSuccess)
     return FA_ERR_LAUNCH;
+  if (fa::launch_bwd_pre(a, stream) != hipSuccess) return FA_ERR_LAUNCH;
+  if (fa::launch_bwd_dkdv(a, stream) != hipSuccess) return FA_ERR_LAUNCH;
+  if (fa::launch_bwd_dq(a, stream) != hipSuccess) return FA_ERR_LAUNCH;
+  return FA_OK;
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------------------------------
+// fa_bwd_noalloc: fa_bwd with its workspace (the fp32 D array) in a fixed device array of this
+// library, for callers that cannot allocate.  Each device holds its own copy of `scratch` from the
+// moment the library's code object is loaded on it until the process ends.  Host code never uses the
+// array's name as a device address: the address of a device's copy is looked up once, with that
+// device current, and kept per device.
+namespace {
+
+constexpr size_t kScratchRows = (size_t)1 << 22;  // D for B·H·N ≤ 2^22 rows: 16 MiB per device
+static __device__ __align__(256) float scratch[kScratchRows];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];  // device address of `scratch` per device; null until looked up
+
+// Device address of `scratch` on the device `stream` belongs to.
+fa_status scratch_address(hipStream_t stream, void** out) {
+  int dev = -1;
+  if (stream == nullptr) {
+    if (hipGetDevice(&dev) != hipSuccess) return FA_ERR_LAUNCH;
+  } else if (hipStreamGetDevice(stream, &dev) != hipSuccess) {
+    return FA_ERR_LAUNCH;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return FA_ERR_LAUNCH;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    int cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess) return FA_ERR_LAUNCH;
+    if (cur != dev && hipSetDevice(dev) != hipSuccess) return FA_ERR_LAUNCH;
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != dev) (void)hipSetDevice(cur);
+    if (e != hipSuccess || p == nullptr) return FA_ERR_LAUNCH;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return FA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t fa_bwd_noalloc_max_rows(void) { return kScratchRows; }
+
+fa_status fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
+                         const float* lse, const void* dout, void* dq, void* dk, void* dv, int B,
+                         int H, int N, int d, int causal, float softmax_scale, hipStream_t stream) {
+  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return FA_ERR_NULL;
+  fa_status st = check_shape(B, H, N, d, 2);
+  if (st != FA_OK) return st;
+  if ((uint64_t)B * (uint64_t)H * (uint64_t)N > (uint64_t)kScratchRows) return FA_ERR_WORKSPACE;
+  if (!good_scale(softmax_scale)) return FA_ERR_UNSUPPORTED;
+  const void* ptrs[] = {q, k, v, o, lse, dout, dq, dk, dv};
+  for (const void* p : ptrs)
+    if (!aligned(p, 16)) return FA_ERR_ALIGN;
+  void* ws = nullptr;
+  st = scratch_address(stream, &ws);
+  if (st != FA_OK) return st;
+  fa::BwdArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.dout = dout;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.delta = (float*)ws;  // every row of D is written by the first kernel before the others read it
+  a.B = B;
+  a.H = H;
+  a.N = N;
+  a.d = d;
+  a.causal = causal ? 1 : 0;
+  a.scale = a.dk_scale = a.dq_scale = softmax_scale;
   if (fa::launch_bwd_pre(a, stream) != hipSuccess) return FA_ERR_LAUNCH;
   if (fa::launch_bwd_dkdv(a, stream) != hipSuccess) return FA_ERR_LAUNCH;
   if (fa::launch_bwd_dq(a, stream) != hipSuccess) return FA_ERR_LAUNCH;

@@ -48,7 +48,7 @@ def test_exports_match_header(lib):
     assert declared == {"fa_fwd", "fa_fwd_fp8", "fa_bwd_workspace_bytes", "fa_bwd", "fa_status_str",
                         "fa_bwd_preprocess", "fa_bwd_dkdv", "fa_bwd_dq", "fa_device_info",
                         "fa_decode", "fa_decode_workspace_bytes", "fa_bwd_fp8",
-                        "fa_bwd_fp8_workspace_bytes"}
+                        "fa_bwd_fp8_workspace_bytes", "fa_bwd_noalloc", "fa_bwd_noalloc_max_rows"}
     for name in declared:
         assert hasattr(lib, name), name
 
@@ -257,3 +257,24 @@ def test_binding_rejects_mixed_devices_without_a_gpu():
         with pytest.raises(ValueError):
             call()
 
+
+def test_noalloc_rejections(lib):
+    """fa_bwd_noalloc checks its arguments before any HIP call: NULL pointers, shapes, the capacity of
+    its fixed device array (B·H·N ≤ 2^22 rows), the scale and alignment."""
+    vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    lib.fa_bwd_noalloc.argtypes = [vp] * 9 + [i, i, i, i, i, f, vp]
+    lib.fa_bwd_noalloc.restype = i
+    lib.fa_bwd_noalloc_max_rows.restype = ctypes.c_size_t
+    assert lib.fa_bwd_noalloc_max_rows() == 1 << 22
+
+    def call(ptrs=None, B=1, H=1, N=64, d=64, scale=0.125):
+        ptrs = ptrs or [P] * 9
+        return lib.fa_bwd_noalloc(*ptrs, B, H, N, d, 1, scale, None)
+
+    assert call(ptrs=[P] * 8 + [None]) == NULL
+    assert call(N=0) == SHAPE
+    assert call(d=80) == UNSUP
+    assert call(B=2, H=2, N=(1 << 20) + 1) == WORKSPACE
+    assert call(H=1024, N=4097) == WORKSPACE
+    assert call(scale=0.0) == UNSUP
+    assert call(ptrs=[P] * 8 + [MIS]) == ALIGN
