@@ -1,8 +1,9 @@
 #!/usr/bin/env python3
 """Throughput of exact attention forward + backward on one MI355X, through the C ABI.
 
-One step is one pass of the whole path over one batch: fa_fwd, then the three backward phases
-(fa_bwd_preprocess, fa_bwd_dkdv, fa_bwd_dq), with every input already resident in device memory.
+One step is one pass of the whole path over one batch: fa_fwd, then the backward's two phases as
+fa_bwd runs them (fa_bwd_delta_dq: D = dO·O and dQ; fa_bwd_dkdv: dK and dV), with every input
+already resident in device memory.
 FLOPs follow the usual convention: forward 4·B·H·N²·d (halved when causal), backward 2.5× the
 forward.  W untimed warm-up steps, then exactly K timed steps between two device
 synchronisations; HIP events on the launch stream give each kernel's own duration.
@@ -352,8 +353,8 @@ def fp8_backward(fa, workloads, lib, steps, warmup):
     fwd_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / steps
     bwd_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / steps
     fwd_f, bwd_f = w.fwd_flops(), w.bwd_flops()
-    out = {"workload": w.name, "kernels": ["e4m3_to_bf16_kernel", "bwd_pre_kernel",
-                                           "bwd_dkdv_kernel", "bwd_dq_kernel"],
+    out = {"workload": w.name, "kernels": ["e4m3_to_bf16_kernel", "bwd_dq_kernel",
+                                           "bwd_dkdv_kernel"],
            "bwd_ms": bwd_ms, "bwd_tflops": bwd_f / (bwd_ms * 1e-3) / 1e12, "fwd_ms": fwd_ms,
            "step_tflops": (fwd_f + bwd_f) / ((fwd_ms + bwd_ms) * 1e-3) / 1e12,
            "bound": "mfma", "peak": BF16_PEAK_TFLOPS, "flops": bwd_f,
@@ -393,34 +394,32 @@ def fwd_bwd_secondary(fa, workloads, lib, name, steps, warmup):
         check("fa_fwd", lib.fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
                                    lse.data_ptr(), B, H, N, d, c, w.scale, sp))
         ev[1].record(stream)
-        check("fa_bwd_preprocess", lib.fa_bwd_preprocess(o.data_ptr(), do.data_ptr(), ws.data_ptr(),
-                                                         ws_bytes, B, H, N, d, sp))
+        check("fa_bwd_delta_dq", lib.fa_bwd_delta_dq(q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                                     o.data_ptr(), lse.data_ptr(), do.data_ptr(),
+                                                     dq.data_ptr(), ws.data_ptr(), ws_bytes, B, H,
+                                                     N, d, c, w.scale, sp))
         ev[2].record(stream)
         check("fa_bwd_dkdv", lib.fa_bwd_dkdv(q.data_ptr(), k.data_ptr(), v.data_ptr(),
                                              lse.data_ptr(), do.data_ptr(), dk.data_ptr(),
                                              dv.data_ptr(), ws.data_ptr(), ws_bytes, B, H, N, d, c,
                                              w.scale, sp))
         ev[3].record(stream)
-        check("fa_bwd_dq", lib.fa_bwd_dq(q.data_ptr(), k.data_ptr(), v.data_ptr(), lse.data_ptr(),
-                                         do.data_ptr(), dq.data_ptr(), ws.data_ptr(), ws_bytes, B,
-                                         H, N, d, c, w.scale, sp))
-        ev[4].record(stream)
 
-    spare = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+    spare = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
     for _ in range(warmup):
         step(spare)
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
     for i in range(steps):
         step(events[i])
     torch.cuda.synchronize(dev)
-    ph = [sum(e[i].elapsed_time(e[i + 1]) for e in events) / steps for i in range(4)]
-    step_ms = sum(e[0].elapsed_time(e[4]) for e in events) / steps
+    ph = [sum(e[i].elapsed_time(e[i + 1]) for e in events) / steps for i in range(3)]
+    step_ms = sum(e[0].elapsed_time(e[3]) for e in events) / steps
     fwd_f, bwd_f = w.fwd_flops(), w.bwd_flops()
     out = {"workload": name, "ms": step_ms, "tflops": (fwd_f + bwd_f) / (step_ms * 1e-3) / 1e12,
            "peak": BF16_PEAK_TFLOPS, "bound": "mfma", "flops": fwd_f + bwd_f,
-           "phases_ms": {"fwd": ph[0], "bwd_preprocess": ph[1], "bwd_dkdv": ph[2], "bwd_dq": ph[3]},
+           "phases_ms": {"fwd": ph[0], "bwd_delta_dq": ph[1], "bwd_dkdv": ph[2]},
            "fwd_tflops": fwd_f / (ph[0] * 1e-3) / 1e12,
-           "bwd_tflops": bwd_f / ((ph[1] + ph[2] + ph[3]) * 1e-3) / 1e12}
+           "bwd_tflops": bwd_f / ((ph[1] + ph[2]) * 1e-3) / 1e12}
     out["frac"] = out["tflops"] / BF16_PEAK_TFLOPS
     del q, k, v, do, o, dq, dk, dv, lse, ws
     torch.cuda.empty_cache()
@@ -511,8 +510,10 @@ def main():
                                    lse.data_ptr(), B, H, N, d, causal, scale, sp))
         if ev is not None:
             ev[1].record(stream)
-        check("fa_bwd_preprocess", lib.fa_bwd_preprocess(o.data_ptr(), do.data_ptr(), ws.data_ptr(),
-                                                         ws_bytes, B, H, N, d, sp))
+        check("fa_bwd_delta_dq", lib.fa_bwd_delta_dq(q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                                     o.data_ptr(), lse.data_ptr(), do.data_ptr(),
+                                                     dq.data_ptr(), ws.data_ptr(), ws_bytes, B, H,
+                                                     N, d, causal, scale, sp))
         if ev is not None:
             ev[2].record(stream)
         check("fa_bwd_dkdv", lib.fa_bwd_dkdv(q.data_ptr(), k.data_ptr(), v.data_ptr(),
@@ -521,18 +522,13 @@ def main():
                                              causal, scale, sp))
         if ev is not None:
             ev[3].record(stream)
-        check("fa_bwd_dq", lib.fa_bwd_dq(q.data_ptr(), k.data_ptr(), v.data_ptr(), lse.data_ptr(),
-                                         do.data_ptr(), dq.data_ptr(), ws.data_ptr(), ws_bytes, B,
-                                         H, N, d, causal, scale, sp))
-        if ev is not None:
-            ev[4].record(stream)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize(dev)
     log(f"[bench] warm-up done ({args.warmup} steps)")
 
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     torch.cuda.synchronize(dev)
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -548,9 +544,8 @@ def main():
     def avg(a, b):
         return sum(durations(a, b)) / len(events)
 
-    fwd_ms, pre_ms, dkdv_ms, dq_ms = avg(0, 1), avg(1, 2), avg(2, 3), avg(3, 4)
-    spans = {"fwd_bf16_kernel": (0, 1), "bwd_pre_kernel": (1, 2), "bwd_dkdv_kernel": (2, 3),
-             "bwd_dq_kernel": (3, 4)}
+    fwd_ms, dq_ms, dkdv_ms = avg(0, 1), avg(1, 2), avg(2, 3)
+    spans = {"fwd_bf16_kernel": (0, 1), "bwd_dq_kernel": (1, 2), "bwd_dkdv_kernel": (2, 3)}
     fwd_f, bwd_f = w.fwd_flops(), w.bwd_flops()
     value = (fwd_f + bwd_f) / (ms_per_step * 1e-3) / 1e12
 
@@ -560,12 +555,11 @@ def main():
 
     # Algorithmic FLOPs per launch: the forward's 2 products; the backward's 5 counted products split
     # as dK/dV kernel = S, dP, dV, dK (4 of 5) and dQ kernel = dQ (1 of 5) — the dQ kernel's two
-    # recomputed products (S, dP) are extra work, not counted.
+    # recomputed products (S, dP) are extra work, not counted, and so is its D = dO·O per query.
     kernels = {
         "fwd_bf16_kernel": {"ms": fwd_ms, "flops": fwd_f, "src": "fa_fwd.hip"},
         "bwd_dkdv_kernel": {"ms": dkdv_ms, "flops": bwd_f * 4 / 5, "src": "fa_bwd.hip"},
         "bwd_dq_kernel": {"ms": dq_ms, "flops": bwd_f * 1 / 5, "src": "fa_bwd.hip"},
-        "bwd_pre_kernel": {"ms": pre_ms, "src": "fa_bwd.hip"},
     }
     for name, kk in kernels.items():
         dd = durations(*spans[name])
@@ -634,10 +628,9 @@ def main():
         "config": {"workload": w.name, "B": B, "H": H, "N": N, "d": d, "causal": w.causal,
                    "softmax_scale": scale, "flops_per_step": fwd_f + bwd_f},
         "mfma_peak_frac": value / BF16_PEAK_TFLOPS,
-        "phases_ms": {"fwd": fwd_ms, "bwd_preprocess": pre_ms, "bwd_dkdv": dkdv_ms,
-                      "bwd_dq": dq_ms},
+        "phases_ms": {"fwd": fwd_ms, "bwd_delta_dq": dq_ms, "bwd_dkdv": dkdv_ms},
         "fwd_tflops": fwd_f / (fwd_ms * 1e-3) / 1e12,
-        "bwd_tflops": bwd_f / ((pre_ms + dkdv_ms + dq_ms) * 1e-3) / 1e12,
+        "bwd_tflops": bwd_f / ((dkdv_ms + dq_ms) * 1e-3) / 1e12,
         "kernels": {n: {k2: v2 for k2, v2 in kk.items() if k2 != "src"} for n, kk in kernels.items()},
         "roofline": roofline,
         "device": device,

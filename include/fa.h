@@ -97,12 +97,18 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
                  int B, int H, int N, int d, int causal, float softmax_scale, hipStream_t stream);
 
 /*
- * The backward pass as its three phases, for callers that schedule or time them separately.
- * fa_bwd enqueues exactly these three calls in this order; arguments mean what they mean there and
- * are checked the same way.  The last two both depend only on the first.
+ * The backward pass in phases, for callers that schedule or time them separately.  Arguments mean
+ * what they mean for fa_bwd and are checked the same way.
  *   fa_bwd_preprocess  D_i = dO_i · O_i (fp32) into the workspace.
- *   fa_bwd_dkdv        recomputes S and P per key tile (key/value-stationary) and writes dK and dV.
- *   fa_bwd_dq          recomputes S, P and dP per query tile (query-stationary) and writes dQ.
+ *   fa_bwd_dkdv        recomputes S and P per key tile (key/value-stationary) and writes dK and dV;
+ *                      needs D in the workspace.
+ *   fa_bwd_dq          recomputes S, P and dP per query tile (query-stationary) and writes dQ; needs
+ *                      D in the workspace.
+ *   fa_bwd_delta_dq    D into the workspace and dQ, bit for bit what fa_bwd_preprocess followed by
+ *                      fa_bwd_dq give; for d ∈ {64, 128, 256} one kernel (each query tile forms its
+ *                      own rows' D from O and dO), for d = 96 those two calls.
+ * fa_bwd enqueues fa_bwd_delta_dq, then fa_bwd_dkdv; fa_bwd_preprocess, fa_bwd_dkdv, fa_bwd_dq in
+ * that order (or with the last two swapped) give the same gradients bit for bit.
  */
 fa_status fa_bwd_preprocess(const void* o, const void* dout, void* workspace, size_t workspace_bytes,
                             int B, int H, int N, int d, hipStream_t stream);
@@ -114,6 +120,10 @@ fa_status fa_bwd_dq(const void* q, const void* k, const void* v, const float* ls
                     const void* dout, void* dq, const void* workspace, size_t workspace_bytes,
                     int B, int H, int N, int d, int causal, float softmax_scale,
                     hipStream_t stream);
+fa_status fa_bwd_delta_dq(const void* q, const void* k, const void* v, const void* o,
+                          const float* lse, const void* dout, void* dq, void* workspace,
+                          size_t workspace_bytes, int B, int H, int N, int d, int causal,
+                          float softmax_scale, hipStream_t stream);
 
 /*
  * Backward pass of the FP8 forward (fa_fwd_fp8): the gradients of O = softmax(scale · Q Kᵀ) V with

@@ -10,7 +10,8 @@ Entry points (same names as the C ABI, without the ``fa_`` prefix):
   fwd_fp8(q8, k8, v8, q_descale, k_descale, v_descale, causal, scale=None) -> (o, lse)
   bwd(q, k, v, o, lse, dout, causal, scale=None, workspace=None) -> (dq, dk, dv)
   bwd_workspace_bytes(B, H, N, d) -> int
-  bwd_preprocess / bwd_dkdv / bwd_dq — the three phases fa_bwd runs, for timing them apart
+  bwd_preprocess / bwd_dkdv / bwd_dq / bwd_delta_dq — the backward's phases (fa_bwd runs
+      bwd_delta_dq, then bwd_dkdv), for scheduling or timing them apart
   bwd_fp8(q8, k8, v8, q_descale, k_descale, v_descale, o, lse, dout, causal, scale=None,
           workspace=None) -> (dq, dk, dv)      (the backward of fwd_fp8)
   bwd_fp8_workspace_bytes(B, H, N, d) -> int
@@ -27,7 +28,8 @@ import os
 import torch
 
 __all__ = ["fwd", "fwd_fp8", "bwd", "bwd_workspace_bytes", "bwd_preprocess", "bwd_dkdv",
-           "bwd_dq", "bwd_fp8", "bwd_fp8_workspace_bytes", "decode", "decode_workspace_bytes",
+           "bwd_dq", "bwd_delta_dq", "bwd_fp8", "bwd_fp8_workspace_bytes", "decode",
+           "decode_workspace_bytes",
            "status_str", "device_info", "FaError", "library", "LIB_PATH"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
@@ -69,6 +71,8 @@ def library():
         lib.fa_bwd_dkdv.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, f, vp]
         lib.fa_bwd_dkdv.restype = i
         lib.fa_bwd_dq.argtypes = [vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, f, vp]
+        lib.fa_bwd_delta_dq.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, f, vp]
+        lib.fa_bwd_delta_dq.restype = i
         lib.fa_bwd_dq.restype = i
         lib.fa_status_str.argtypes = [i]
         lib.fa_status_str.restype = ctypes.c_char_p
@@ -307,3 +311,15 @@ def bwd_dq(q, k, v, lse, dout, dq, workspace, causal, scale=None):
                                    workspace.numel(), B, H, N, d, int(bool(causal)),
                                    _scale(scale, d), _stream(q.device))
     _check("fa_bwd_dq", code)
+
+
+def bwd_delta_dq(q, k, v, o, lse, dout, dq, workspace, causal, scale=None):
+    """D into the workspace and dq in one phase (what bwd_preprocess then bwd_dq give, bit for bit);
+    bwd_dkdv on the same workspace may follow."""
+    B, H, N, d = _bwd_inputs(q, k, v, lse, dout, workspace, ((o, "o"), (dq, "dq")))
+    with torch.cuda.device(q.device):
+        code = library().fa_bwd_delta_dq(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                         lse.data_ptr(), dout.data_ptr(), dq.data_ptr(),
+                                         workspace.data_ptr(), workspace.numel(), B, H, N, d,
+                                         int(bool(causal)), _scale(scale, d), _stream(q.device))
+    _check("fa_bwd_delta_dq", code)

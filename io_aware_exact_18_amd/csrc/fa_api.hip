@@ -172,6 +172,28 @@ fa_status fa_bwd_dq(const void* q, const void* k, const void* v, const float* ls
   return fa::launch_bwd_dq(a, stream) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
+fa_status fa_bwd_delta_dq(const void* q, const void* k, const void* v, const void* o,
+                          const float* lse, const void* dout, void* dq, void* workspace,
+                          size_t workspace_bytes, int B, int H, int N, int d, int causal,
+                          float softmax_scale, hipStream_t stream) {
+  if (!q || !k || !v || !o || !lse || !dout || !dq) return FA_ERR_NULL;
+  fa::BwdArgs a{};
+  const void* ptrs[] = {q, k, v, o, lse, dout, dq};
+  fa_status st = check_bwd(ptrs, 7, workspace, workspace_bytes, B, H, N, d, &a);
+  if (st != FA_OK) return st;
+  if (!good_scale(softmax_scale)) return FA_ERR_UNSUPPORTED;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.dout = dout;
+  a.dq = dq;
+  a.causal = causal ? 1 : 0;
+  a.scale = a.dk_scale = a.dq_scale = softmax_scale;
+  return fa::launch_bwd_delta_dq(a, stream) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
 }  // extern "C"
 
 namespace {
@@ -233,10 +255,7 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
   a.dv = dv;
   a.causal = causal ? 1 : 0;
   a.scale = a.dk_scale = a.dq_scale = softmax_scale;
-  if (fa::launch_bwd_pre(a, stream) != hipSuccess) return FA_ERR_LAUNCH;
-  if (fa::launch_bwd_dkdv(a, stream) != hipSuccess) return FA_ERR_LAUNCH;
-  if (fa::launch_bwd_dq(a, stream) != hipSuccess) return FA_ERR_LAUNCH;
-  return FA_OK;
+  return fa::launch_bwd(a, stream) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
 size_t fa_bwd_fp8_workspace_bytes(int B, int H, int N, int d) {
@@ -290,10 +309,7 @@ fa_status fa_bwd_fp8(const void* q8, const void* k8, const void* v8, float q_des
       fa::launch_e4m3_to_bf16(k8, kc, n, stream) != hipSuccess ||
       fa::launch_e4m3_to_bf16(v8, vc, n, stream) != hipSuccess)
     return FA_ERR_LAUNCH;
-  if (fa::launch_bwd_pre(a, stream) != hipSuccess) return FA_ERR_LAUNCH;
-  if (fa::launch_bwd_dkdv(a, stream) != hipSuccess) return FA_ERR_LAUNCH;
-  if (fa::launch_bwd_dq(a, stream) != hipSuccess) return FA_ERR_LAUNCH;
-  return FA_OK;
+  return fa::launch_bwd(a, stream) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
 }  // extern "C"
@@ -374,10 +390,7 @@ fa_status fa_bwd_noalloc(const void* q, const void* k, const void* v, const void
   a.d = d;
   a.causal = causal ? 1 : 0;
   a.scale = a.dk_scale = a.dq_scale = softmax_scale;
-  if (fa::launch_bwd_pre(a, stream) != hipSuccess) return FA_ERR_LAUNCH;
-  if (fa::launch_bwd_dkdv(a, stream) != hipSuccess) return FA_ERR_LAUNCH;
-  if (fa::launch_bwd_dq(a, stream) != hipSuccess) return FA_ERR_LAUNCH;
-  return FA_OK;
+  return fa::launch_bwd(a, stream) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
 }  // extern "C"

@@ -8,11 +8,12 @@
 //   dK = scale · dSᵀ Q.
 // D_i equals Σ_j P_ij dP_ij (the row term of the softmax Jacobian) because O_i = Σ_j P_ij V_j.
 //
-// Three launches on the caller's stream, none with atomics:
-//   1. bwd_pre: D_i = dO_i · O_i in fp32 (workspace).
+// Launches on the caller's stream, none with atomics (launch_bwd: D and dQ, then dK/dV):
+//   1. bwd_pre: D_i = dO_i · O_i in fp32 (workspace), or inside the dQ kernel (see there).
 //   2. bwd_dkdv: key/value-stationary.  One workgroup per 128 keys (4 waves × 32 keys).  Each wave
 //      keeps its K rows as matrix-core operands and its dKᵀ, dVᵀ accumulators in registers (V rows
-//      stay in LDS) and walks the 32-query tiles the causal mask allows, staged in LDS by direct
+//      stay in LDS) and walks the 32-query tiles the causal mask allows, from the last one down (all
+//      key blocks of a head then share each Q/dO tile through L2), staged in LDS by direct
 //      buffer→LDS copies (double-buffered, one barrier per tile).  Per tile: S = Q Kᵀ and
 //      dP = dO Vᵀ (32×32×16 bf16 matrix cores, Q and dO rows from LDS), P and dS on the vector
 //      units, then dVᵀ += dOᵀ P and dKᵀ += Qᵀ dS with transposed LDS reads supplying dOᵀ and Qᵀ.
@@ -139,13 +140,18 @@ __global__ __launch_bounds__(kThreads, (D == 256 && OUT != 1) ? 1 : 2) void bwd_
   const FragOffsets<L> fo(lane);
   const int qstart = CAUSAL ? k0 : 0;  // causal: only queries ≥ the tile's first key
   const int nsteps = (N - qstart + kBQ - 1) / kBQ;
+  // Query tiles are walked from the last one down to qstart: every workgroup of a head starts on the
+  // same tiles and they move through Q and dO together, so each tile is read from memory about once
+  // and then served from L2 to the head's other key blocks (ascending, the key blocks would start at
+  // their own diagonals and keep all of the head's Q and dO in use at once).
+  auto step_q = [&](int step) { return qstart + (nsteps - 1 - step) * kBQ; };
 
   // Q, dO and D of query step `step` go to LDS by DMA; wave 0 also loads the step's LSE into a
   // register and stores it, times log2(e), to LDS just before the step's closing barrier, so the
   // probabilities below are one FMA and one exp2 each.
   float lse_next = 0.f;
   auto stage = [&](int step, bf16* qd, bf16* od, float* dd) {
-    const int qb = qstart + step * kBQ;
+    const int qb = step_q(step);
     copy(mq, qb, qd);
     copy(mdo, qb, od);
     if (wave == 0) lse_next = __uint_as_float(buf_load4(rlse, (uint32_t)(qb + lane) * 4u));
@@ -175,7 +181,7 @@ __global__ __launch_bounds__(kThreads, (D == 256 && OUT != 1) ? 1 : 2) void bwd_
     const float* lse_s = P ? l1s : l0s;
     const float* del_s = P ? d1s : d0s;
     if (step + 1 < nsteps) stage(step + 1, P ? q0s : q1s, P ? o0s : o1s, P ? d0s : d1s);
-    const int qb = qstart + step * kBQ;
+    const int qb = step_q(step);
 
     if (!(CAUSAL && kw > qb + kBQ - 1)) {  // every (query, key) pair masked for this wave: skip
       // S = Q Kᵀ and dP = dO Vᵀ for 32 queries × this wave's 32 keys.
@@ -266,12 +272,20 @@ __global__ __launch_bounds__(kThreads, (D == 256 && OUT != 1) ? 1 : 2) void bwd_
 }
 
 // ---------------------------------------------------------------------------------------------------
-// 3. dQ.
-template <int D, bool CAUSAL>
+// 3. dQ.  WITH_D: the kernel also forms D_i = dO_i · O_i for its own queries (each lane holds its
+// query's dO fragments already; O is read once in the same layout) and writes it for the dK/dV kernel,
+// in place of the separate bwd_pre launch.  The sum takes bwd_pre's order exactly (runs of 8 products,
+// then the same pairwise tree), so D, and every gradient, is bit for bit what bwd_pre gives: bwd_pre's
+// thread t of a row sums d values 8t .. 8t + 7, here chunk (s, g) of lane (query, g), t = 2s + g, so its
+// tree levels t ^ 2h are in-lane (s ^ h) and t ^ 1 is the other half-wave.  Head dimension 96 (runs of
+// 24 values per bwd_pre thread, which straddle the half-waves) keeps the separate launch.
+template <int D, bool CAUSAL, bool WITH_D>
 __global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void bwd_dq_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
-    const float* __restrict__ LSE, const bf16* __restrict__ dO, const float* __restrict__ Delta,
-    bf16* __restrict__ dQ, int N, int nqt, float scale, float scale_log2, int remap) {
+    const float* __restrict__ LSE, const bf16* __restrict__ dO, float* __restrict__ Delta,
+    const bf16* __restrict__ O, bf16* __restrict__ dQ, int N, int nqt, float scale,
+    float scale_log2, float delta_mult, int remap) {
+  static_assert(!WITH_D || pre_tpr<D>() == D / 8, "D in the dQ kernel: runs of 8 values");
   constexpr int KSTEPS = D / 16;
   constexpr int DB = D / 32;
   constexpr int L = lds_cols<D>();
@@ -313,9 +327,37 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void bwd_dq_kernel(
     df[s] = __builtin_bit_cast(bf16x8, buf_load16(rdo, off));
   }
   const auto rlse = make_rsrc(LSE + (size_t)bh * N, (uint32_t)N * 4u);
-  const auto rdel = make_rsrc(Delta + (size_t)bh * N, (uint32_t)N * 4u);
   const float lse2 = __uint_as_float(buf_load4(rlse, (uint32_t)qi * 4u)) * kLog2e;
-  const float dlt = __uint_as_float(buf_load4(rdel, (uint32_t)qi * 4u));
+  float dlt;
+  if constexpr (WITH_D) {
+    const auto ro = make_rsrc(O + head, head_bytes);
+    float c[KSTEPS];  // chunk sums, then the tree's partial sums
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s) {
+      const u32x4 ov = buf_load16(ro, (uint32_t)(qi * D + 16 * s + 8 * g) * 2u);
+      const u32x4 dv = __builtin_bit_cast(u32x4, df[s]);
+      float acc = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc = fmaf(bf16_bits_to_float(ov[i] & 0xffffu), bf16_bits_to_float(dv[i] & 0xffffu), acc);
+        acc = fmaf(bf16_bits_to_float(ov[i] >> 16), bf16_bits_to_float(dv[i] >> 16), acc);
+      }
+      c[s] = acc;
+    }
+#pragma unroll
+    for (int h = KSTEPS / 2; h > 0; h >>= 1) {
+      float nc[KSTEPS];
+#pragma unroll
+      for (int s = 0; s < KSTEPS; ++s) nc[s] = c[s] + c[s ^ h];
+#pragma unroll
+      for (int s = 0; s < KSTEPS; ++s) c[s] = nc[s];
+    }
+    dlt = halves_sum(c[0]) * delta_mult;
+    if (g == 0 && qi < N) Delta[(size_t)bh * N + qi] = dlt;
+  } else {
+    const auto rdel = make_rsrc(Delta + (size_t)bh * N, (uint32_t)N * 4u);
+    dlt = __uint_as_float(buf_load4(rdel, (uint32_t)qi * 4u));
+  }
 
   const int kv_end = CAUSAL ? min(N, q0 + kBR) : N;
   const int ntiles = (kv_end + kBC - 1) / kBC;
@@ -447,16 +489,21 @@ hipError_t launch_dkdv(const BwdArgs& a, hipStream_t stream) {
   }
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool WITH_D>
 hipError_t launch_dq(const BwdArgs& a, hipStream_t stream) {
   const int nqt = (a.N + kBR - 1) / kBR;
   const uint32_t total = (uint32_t)a.B * a.H * nqt;
   const int remap = use_xcd_order(total, (long)a.B * a.H, CAUSAL ? 1 : 0);
-  hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3(total), dim3(kThreads), 0, stream,
+  hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, WITH_D>), dim3(total), dim3(kThreads), 0, stream,
                      (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, a.lse,
-                     (const bf16*)a.dout, (const float*)a.delta, (bf16*)a.dq, a.N, nqt, a.dq_scale,
-                     a.scale * kLog2e, remap);
+                     (const bf16*)a.dout, a.delta, (const bf16*)a.o, (bf16*)a.dq, a.N, nqt,
+                     a.dq_scale, a.scale * kLog2e, a.delta_mult, remap);
   return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_dq_with_d(const BwdArgs& a, hipStream_t stream) {
+  return a.causal ? launch_dq<D, true, true>(a, stream) : launch_dq<D, false, true>(a, stream);
 }
 
 }  // namespace
@@ -479,11 +526,26 @@ hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t stream) {
 }
 
 hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t stream) {
-  if (a.d == 64) return a.causal ? launch_dq<64, true>(a, stream) : launch_dq<64, false>(a, stream);
-  if (a.d == 96) return a.causal ? launch_dq<96, true>(a, stream) : launch_dq<96, false>(a, stream);
+  if (a.d == 64)
+    return a.causal ? launch_dq<64, true, false>(a, stream) : launch_dq<64, false, false>(a, stream);
+  if (a.d == 96)
+    return a.causal ? launch_dq<96, true, false>(a, stream) : launch_dq<96, false, false>(a, stream);
   if (a.d == 256)
-    return a.causal ? launch_dq<256, true>(a, stream) : launch_dq<256, false>(a, stream);
-  return a.causal ? launch_dq<128, true>(a, stream) : launch_dq<128, false>(a, stream);
+    return a.causal ? launch_dq<256, true, false>(a, stream) : launch_dq<256, false, false>(a, stream);
+  return a.causal ? launch_dq<128, true, false>(a, stream) : launch_dq<128, false, false>(a, stream);
+}
+
+hipError_t launch_bwd_delta_dq(const BwdArgs& a, hipStream_t stream) {
+  if (a.d == 64) return launch_dq_with_d<64>(a, stream);
+  if (a.d == 128) return launch_dq_with_d<128>(a, stream);
+  if (a.d == 256) return launch_dq_with_d<256>(a, stream);
+  const hipError_t e = launch_bwd_pre(a, stream);
+  return e == hipSuccess ? launch_bwd_dq(a, stream) : e;
+}
+
+hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream) {
+  const hipError_t e = launch_bwd_delta_dq(a, stream);
+  return e == hipSuccess ? launch_bwd_dkdv(a, stream) : e;
 }
 
 }  // namespace fa

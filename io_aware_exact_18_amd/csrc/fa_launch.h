@@ -103,6 +103,11 @@ hipError_t launch_fwd_fp8(const Fp8FwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd_pre(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t stream);
+// D into the workspace and dQ: one kernel where the head dimension allows (D formed inside the dQ
+// kernel), else launch_bwd_pre then launch_bwd_dq; bit for bit the same results either way.
+hipError_t launch_bwd_delta_dq(const BwdArgs& a, hipStream_t stream);
+// The whole backward: launch_bwd_delta_dq, then launch_bwd_dkdv.
+hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 // n e4m3fn codes (n a multiple of 16, both pointers 16-byte aligned) → n bf16 values equal to the
 // codes' values (exact: every e4m3 value is a bf16 value).

@@ -48,7 +48,8 @@ def test_exports_match_header(lib):
     assert declared == {"fa_fwd", "fa_fwd_fp8", "fa_bwd_workspace_bytes", "fa_bwd", "fa_status_str",
                         "fa_bwd_preprocess", "fa_bwd_dkdv", "fa_bwd_dq", "fa_device_info",
                         "fa_decode", "fa_decode_workspace_bytes", "fa_bwd_fp8",
-                        "fa_bwd_fp8_workspace_bytes", "fa_bwd_noalloc", "fa_bwd_noalloc_max_rows"}
+                        "fa_bwd_fp8_workspace_bytes", "fa_bwd_noalloc", "fa_bwd_noalloc_max_rows",
+                        "fa_bwd_delta_dq"}
     for name in declared:
         assert hasattr(lib, name), name
 

@@ -659,10 +659,11 @@ def test_more_than_2_32_elements_per_tensor():
     torch.cuda.empty_cache()  # hand the ~86 GB back before the tests that follow
 
 
-@pytest.mark.parametrize("d", [96, 128, 256])
+@pytest.mark.parametrize("d", [64, 96, 128, 256])
 def test_bwd_phases_equal_fused_call(d):
-    """fa_bwd_preprocess + fa_bwd_dkdv + fa_bwd_dq give bitwise what fa_bwd gives, and fa_bwd is
-    deterministic from run to run."""
+    """fa_bwd (D formed inside the dQ kernel, then dK/dV), fa_bwd_delta_dq + fa_bwd_dkdv, and
+    fa_bwd_preprocess + fa_bwd_dkdv + fa_bwd_dq all give the same gradients bit for bit, the D each
+    leaves in the workspace is bit for bit the same, and fa_bwd is deterministic from run to run."""
     B, H, N = 2, 2, 333
     g = torch.Generator().manual_seed(15)
     q, k, v, do = (torch.randn(B, H, N, d, generator=g).to(torch.bfloat16).cuda() for _ in range(4))
@@ -676,9 +677,15 @@ def test_bwd_phases_equal_fused_call(d):
         fa().bwd_preprocess(o, do, ws)
         fa().bwd_dkdv(q, k, v, lse, do, dk2, dv2, ws, causal, scale)
         fa().bwd_dq(q, k, v, lse, do, dq2, ws, causal, scale)
+        ws3 = torch.full_like(ws, 0x5A)
+        dq3, dk3, dv3 = (torch.empty_like(q) for _ in range(3))
+        fa().bwd_delta_dq(q, k, v, o, lse, do, dq3, ws3, causal, scale)
+        fa().bwd_dkdv(q, k, v, lse, do, dk3, dv3, ws3, causal, scale)
         torch.cuda.synchronize()
-        for a, b in zip((dq, dk, dv), (dq2, dk2, dv2)):
-            assert torch.equal(a, b)
+        n_d = B * H * N * 4
+        assert torch.equal(ws[:n_d], ws3[:n_d])
+        for a, b, c in zip((dq, dk, dv), (dq2, dk2, dv2), (dq3, dk3, dv3)):
+            assert torch.equal(a, b) and torch.equal(a, c)
         for a, b in zip((dq, dk, dv), again):
             assert torch.equal(a, b)
 
