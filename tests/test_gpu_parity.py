@@ -428,7 +428,9 @@ def test_workload_fwd_small_full():
     inp = workloads.make_inputs("fwd_small")
     o, lse = _run_fwd(inp["q"], inp["k"], inp["v"], w.causal, w.scale)
     assert tuple(o.shape) == (1, 2, 256, 64) and tuple(lse.shape) == (1, 2, 256)
-    _check_fwd_heads(inp["q"], inp["k"], inp["v"], o.cpu(), lse.cpu(), w.causal, w.scale)
+    e_o, e_l = _check_fwd_heads(inp["q"], inp["k"], inp["v"], o.cpu(), lse.cpu(), w.causal, w.scale)
+    print(f"\nPARITY fwd_small: O {e_o:.4g} LSE {e_l:.3g} (forward: 2 heads; O bound 1e-2)",
+          flush=True)
 
 
 @pytest.mark.parametrize("name", ["d64_2k", "causal_4k", "long_16k", "d256_4k", "d96_4k"])
