@@ -99,7 +99,8 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
 /*
  * The backward pass in phases, for callers that schedule or time them separately.  Arguments mean
  * what they mean for fa_bwd and are checked the same way.
- *   fa_bwd_preprocess  D_i = dO_i · O_i (fp32) into the workspace.
+ *   fa_bwd_preprocess  D_i = dO_i · O_i (fp32) into the workspace (stored as −D_i; the layout of
+ *                      the workspace is internal to these calls).
  *   fa_bwd_dkdv        recomputes S and P per key tile (key/value-stationary) and writes dK and dV;
  *                      needs D in the workspace.
  *   fa_bwd_dq          recomputes S, P and dP per query tile (query-stationary) and writes dQ; needs

@@ -9,7 +9,9 @@
 // D_i equals Σ_j P_ij dP_ij (the row term of the softmax Jacobian) because O_i = Σ_j P_ij V_j.
 //
 // Launches on the caller's stream, none with atomics (launch_bwd: D and dQ, then dK/dV):
-//   1. bwd_pre: D_i = dO_i · O_i in fp32 (workspace), or inside the dQ kernel (see there).
+//   1. bwd_pre: D_i = dO_i · O_i in fp32, or inside the dQ kernel (see there).  The workspace holds
+//      −D_i: the dK/dV kernel starts each dP accumulation from the step's −D values, so dP − D needs
+//      no subtraction.
 //   2. bwd_dkdv: key/value-stationary.  One workgroup per 128 keys (4 waves × 32 keys).  Each wave
 //      keeps its K rows as matrix-core operands and its dKᵀ, dVᵀ accumulators in registers (V rows
 //      stay in LDS) and walks the 32-query tiles the causal mask allows, from the last one down (all
@@ -41,8 +43,8 @@ constexpr int kBR = 128;   // dQ kernel: queries per workgroup (32 per wave)
 constexpr int kBC = 64;    // dQ kernel: keys per tile
 
 // ---------------------------------------------------------------------------------------------------
-// 1. D_i = Σ_t dO_it O_it.  One row per pre_tpr<D>() threads (a power of two), each summing
-// D / (8·TPR) runs of 8 elements.
+// 1. D_i = Σ_t dO_it O_it, stored negated.  One row per pre_tpr<D>() threads (a power of two), each
+// summing D / (8·TPR) runs of 8 elements.
 template <int D>
 constexpr int pre_tpr() { return D == 96 ? 4 : D / 8; }
 
@@ -71,7 +73,7 @@ __global__ __launch_bounds__(kThreads) void bwd_pre_kernel(const bf16* __restric
   }
 #pragma unroll
   for (int off = TPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, TPR);
-  if (row < rows && part == 0) delta[row] = acc * mult;
+  if (row < rows && part == 0) delta[row] = -(acc * mult);
 }
 
 // ---------------------------------------------------------------------------------------------------
@@ -187,9 +189,14 @@ __global__ __launch_bounds__(kThreads, (D == 256 && OUT != 1) ? 1 : 2) void bwd_
       // S = Q Kᵀ and dP = dO Vᵀ for 32 queries × this wave's 32 keys.
       f32x16 sacc, pacc;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        sacc[r] = 0.f;
-        pacc[r] = 0.f;
+      for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
+      if constexpr (WANT_DK) {  // dP accumulates onto −D: element r holds query 8(r/4) + 4g + r%4
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const f32x4 d4 = *(const f32x4*)&del_s[8 * r4 + 4 * g];
+#pragma unroll
+          for (int t = 0; t < 4; ++t) pacc[4 * r4 + t] = d4[t];
+        }
       }
 #pragma unroll
       for (int s = 0; s < KSTEPS; ++s) {
@@ -210,13 +217,12 @@ __global__ __launch_bounds__(kThreads, (D == 256 && OUT != 1) ? 1 : 2) void bwd_
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
         const f32x4 l4 = *(const f32x4*)&lse_s[8 * r4 + 4 * g];
-        const f32x4 d4 = *(const f32x4*)&del_s[8 * r4 + 4 * g];
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
           const int r = 4 * r4 + t;
           const float p = exp2_fast(fmaf(sacc[r], scale_log2, -l4[t]));  // staged LSE is base 2
           sacc[r] = p;
-          if constexpr (WANT_DK) pacc[r] = p * (pacc[r] - d4[t]);  // dS without the scale
+          if constexpr (WANT_DK) pacc[r] = p * pacc[r];  // dS without the scale
         }
       }
       bf16x8 pb[2], dsb[2];  // k-step ks covers queries 16ks + 8(e/4) + 4g + (e%4)
@@ -353,10 +359,10 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void bwd_dq_kernel(
       for (int s = 0; s < KSTEPS; ++s) c[s] = nc[s];
     }
     dlt = halves_sum(c[0]) * delta_mult;
-    if (g == 0 && qi < N) Delta[(size_t)bh * N + qi] = dlt;
+    if (g == 0 && qi < N) Delta[(size_t)bh * N + qi] = -dlt;
   } else {
     const auto rdel = make_rsrc(Delta + (size_t)bh * N, (uint32_t)N * 4u);
-    dlt = __uint_as_float(buf_load4(rdel, (uint32_t)qi * 4u));
+    dlt = -__uint_as_float(buf_load4(rdel, (uint32_t)qi * 4u));
   }
 
   const int kv_end = CAUSAL ? min(N, q0 + kBR) : N;

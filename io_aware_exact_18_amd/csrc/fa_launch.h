@@ -37,7 +37,7 @@ struct BwdArgs {
   void* dq;
   void* dk;
   void* dv;
-  float* delta;  // fp32 [B,H,N] workspace: D_i = (dO_i · O_i) · delta_mult
+  float* delta;  // fp32 [B,H,N] workspace: −D_i, D_i = (dO_i · O_i) · delta_mult
   int B, H, N, d, causal;
   float scale;             // multiplier of the products of q and k as stored (the softmax scale)
   float dk_scale = 0.f;    // dK = dk_scale · Σ_i dS_ij q_i and dQ = dq_scale · Σ_j dS_ij k_j, with
@@ -113,7 +113,7 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 // codes' values (exact: every e4m3 value is a bf16 value).
 hipError_t launch_e4m3_to_bf16(const void* src, void* dst, size_t n, hipStream_t stream);
 
-// Backward workspace: the fp32 [B,H,N] array D, rounded up to 256 bytes.
+// Backward workspace: the fp32 [B,H,N] array of −D, rounded up to 256 bytes.
 inline size_t round_up_256(size_t x) { return (x + 255u) & ~(size_t)255u; }
 inline size_t bwd_delta_bytes(int B, int H, int N) {
   return round_up_256((size_t)B * H * N * sizeof(float));
