@@ -61,6 +61,32 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
                  int B, int H, int N, int d, int causal, float softmax_scale, hipStream_t stream);
 
 /*
+ * Forward pass as fa_fwd, with a workspace that lets the library split each query tile's key range
+ * when B·H·⌈N/128⌉ is too small to fill the device (few heads, long sequences: the long-context case
+ * of "FlashAttention: where it matters", section "Where It Matters").  Each key segment's partial
+ * result (unnormalised output, reference maximum, row sums) goes to the workspace and a second kernel
+ * combines a row's segments by their softmax mass: the recurrence of "Anatomy of a FlashAttention
+ * Kernel", section "What is online softmax and how does tiling keep it exact?", applied to whole key
+ * ranges.  The result is the same attention; it can differ from fa_fwd's in the last bits (another
+ * summation order).
+ *   workspace  device memory of at least fa_fwd_split_workspace_bytes(B, H, N, d, causal) bytes,
+ *              256-byte aligned, owned by the caller, contents undefined after the call.  May be NULL
+ *              when that size is 0: the shape is not split and the call is fa_fwd.
+ * Split rule: with d ≤ 128, T = the number of 64-key tiles summed over every (batch·head, 128-query
+ * tile) pair (under the causal mask a query tile's keys end at its last query) and kt = ⌈N/64⌉, the
+ * shape is split when kt·512 ≥ 4·T, or 2·kt·512 ≥ 3·T and kt ≥ 256 (512: two workgroups on each of the
+ * device's 256 compute units), into segments of seg = min(128, max(16, ⌊kt/8⌋)) tiles, provided seg
+ * < kt; nseg = ⌈kt/seg⌉ segments, and the workspace is nseg·B·H·N·(d + 3) fp32 values rounded up to
+ * 256 bytes.  Otherwise the workspace is 0.
+ * Errors: as fa_fwd; FA_ERR_WORKSPACE when the workspace is needed and NULL or too small,
+ * FA_ERR_ALIGN when it is not 256-byte aligned.  Head dimension 256 is never split.
+ */
+size_t fa_fwd_split_workspace_bytes(int B, int H, int N, int d, int causal);
+fa_status fa_fwd_split(const void* q, const void* k, const void* v, void* o, float* lse,
+                       void* workspace, size_t workspace_bytes, int B, int H, int N, int d,
+                       int causal, float softmax_scale, hipStream_t stream);
+
+/*
  * Forward pass with FP8 matrix products ("Anatomy ...", section "What changed between FlashAttention
  * 1, 2, and 3?": low-precision FP8).  Q, K, V are OCP e4m3fn codes with one fp32 scale per tensor:
  * the value of a code c in tensor X is c · x_descale.  Both products (Q Kᵀ and P V) run on fp8 matrix

@@ -27,7 +27,7 @@ import os
 
 import torch
 
-__all__ = ["fwd", "fwd_fp8", "bwd", "bwd_workspace_bytes", "bwd_preprocess", "bwd_dkdv",
+__all__ = ["fwd", "fwd_split", "fwd_split_workspace_bytes", "fwd_fp8", "bwd", "bwd_workspace_bytes", "bwd_preprocess", "bwd_dkdv",
            "bwd_dq", "bwd_delta_dq", "bwd_fp8", "bwd_fp8_workspace_bytes", "decode",
            "decode_workspace_bytes",
            "status_str", "device_info", "FaError", "library", "LIB_PATH"]
@@ -60,6 +60,10 @@ def library():
         vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
         lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, vp]
         lib.fa_fwd.restype = i
+        lib.fa_fwd_split_workspace_bytes.argtypes = [i, i, i, i, i]
+        lib.fa_fwd_split_workspace_bytes.restype = sz
+        lib.fa_fwd_split.argtypes = [vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, f, vp]
+        lib.fa_fwd_split.restype = i
         lib.fa_fwd_fp8.argtypes = [vp, vp, vp, f, f, f, vp, vp, i, i, i, i, i, f, vp]
         lib.fa_fwd_fp8.restype = i
         lib.fa_bwd_workspace_bytes.argtypes = [i, i, i, i]
@@ -146,6 +150,35 @@ def fwd(q, k, v, causal, scale=None):
                                 lse.data_ptr(), B, H, N, d, int(bool(causal)), _scale(scale, d),
                                 _stream(q.device))
     _check("fa_fwd", code)
+    return o, lse
+
+
+def fwd_split_workspace_bytes(B, H, N, d, causal):
+    """Bytes of workspace fa_fwd_split needs (0: the shape is not split, or is rejected)."""
+    return int(library().fa_fwd_split_workspace_bytes(B, H, N, d, int(bool(causal))))
+
+
+def fwd_split(q, k, v, causal, scale=None, workspace=None):
+    """Forward pass that may split each query tile's key range (fa_fwd_split): returns (o, lse) as
+    fwd.  The workspace (uint8, device) is allocated here when not given."""
+    _require(q, "q", torch.bfloat16)
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, N, d]")
+    _require(k, "k", torch.bfloat16, q.shape, device=q.device)
+    _require(v, "v", torch.bfloat16, q.shape, device=q.device)
+    B, H, N, d = q.shape
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        ws_bytes = fwd_split_workspace_bytes(B, H, N, d, causal)
+        workspace = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=q.device)
+    else:
+        _require(workspace, "workspace", torch.uint8, device=q.device)
+    with torch.cuda.device(q.device):
+        code = library().fa_fwd_split(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                      lse.data_ptr(), workspace.data_ptr(), workspace.numel(), B, H,
+                                      N, d, int(bool(causal)), _scale(scale, d), _stream(q.device))
+    _check("fa_fwd_split", code)
     return o, lse
 
 

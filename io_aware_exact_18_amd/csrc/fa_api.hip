@@ -68,6 +68,28 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
   return fa::launch_fwd_bf16(a, stream) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
+size_t fa_fwd_split_workspace_bytes(int B, int H, int N, int d, int causal) {
+  if (check_shape(B, H, N, d, 2) != FA_OK) return 0;
+  return fa::fwd_split_workspace_bytes(B, H, N, d, causal ? 1 : 0);
+}
+
+fa_status fa_fwd_split(const void* q, const void* k, const void* v, void* o, float* lse,
+                       void* workspace, size_t workspace_bytes, int B, int H, int N, int d,
+                       int causal, float softmax_scale, hipStream_t stream) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+  fa_status st = check_shape(B, H, N, d, 2);
+  if (st != FA_OK) return st;
+  if (!good_scale(softmax_scale)) return FA_ERR_UNSUPPORTED;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 16))
+    return FA_ERR_ALIGN;
+  const size_t need = fa::fwd_split_workspace_bytes(B, H, N, d, causal ? 1 : 0);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return FA_ERR_WORKSPACE;
+  if (need > 0 && !aligned(workspace, 256)) return FA_ERR_ALIGN;
+  fa::FwdArgs a{q, k, v, o, lse, B, H, N, d, causal ? 1 : 0, softmax_scale};
+  a.workspace = need > 0 ? workspace : nullptr;
+  return fa::launch_fwd_bf16(a, stream) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
 fa_status fa_fwd_fp8(const void* q8, const void* k8, const void* v8, float q_descale,
                      float k_descale, float v_descale, void* o, float* lse, int B, int H, int N,
                      int d, int causal, float softmax_scale, hipStream_t stream) {

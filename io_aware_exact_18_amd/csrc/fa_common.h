@@ -263,6 +263,41 @@ __device__ inline void vec64_to_lds(__amdgpu_buffer_rsrc_t r, int e0, float* lds
                                            (uint32_t)(e0 + lane) * 4u, 0, 0, 0);
 }
 
+// Combines `nseg` partial results of one query row, each over a disjoint range of keys, into the row's
+// output and logsumexp: the online-softmax recurrence of "Anatomy of a FlashAttention Kernel", section
+// "What is online softmax and how does tiling keep it exact?", applied to whole key ranges.  Partial s
+// is at row row0 + s·stride of part_o (D fp32: the unnormalised output Σ p·v) and of part_ml (3 fp32:
+// the range's reference maximum m in base 2, and its row sums over the fp32 probabilities and over the
+// same values rounded to bf16).  O is divided by the merged bf16 sum (the weights the products
+// applied), LSE comes from the fp32 sum.  One wave per row: lane t writes columns t, t + 64, ...
+template <int D>
+__device__ inline void merge_partials(const float* __restrict__ part_o,
+                                      const float* __restrict__ part_ml, size_t row0,
+                                      size_t stride, int nseg, bf16* __restrict__ orow,
+                                      float* __restrict__ lse_out, int lane) {
+  constexpr int PER = (D + 63) / 64;  // values per lane (the last partly idle when D = 96)
+  float m = -INFINITY;
+  for (int s = 0; s < nseg; ++s) m = fmaxf(m, part_ml[3 * (row0 + (size_t)s * stride)]);
+  float l = 0.f, lr = 0.f, acc[PER];
+#pragma unroll
+  for (int t = 0; t < PER; ++t) acc[t] = 0.f;
+  for (int s = 0; s < nseg; ++s) {
+    const size_t row = row0 + (size_t)s * stride;
+    const float ms = part_ml[3 * row];
+    const float w = exp2_fast(ms - m);  // 0 for a range without usable keys (ms = -inf)
+    l += w * part_ml[3 * row + 1];
+    lr += w * part_ml[3 * row + 2];
+#pragma unroll
+    for (int t = 0; t < PER; ++t)
+      if (D % 64 == 0 || lane + 64 * t < D) acc[t] += w * part_o[row * D + lane + 64 * t];
+  }
+  const float inv = 1.f / lr;
+#pragma unroll
+  for (int t = 0; t < PER; ++t)
+    if (D % 64 == 0 || lane + 64 * t < D) orow[lane + 64 * t] = (__bf16)(acc[t] * inv);
+  if (lane == 0) *lse_out = (m + __log2f(l)) * kLn2;
+}
+
 // blockIdx → logical work item such that consecutive logical items land on the same XCD: logical
 // item L runs on XCD L / (total / 8).  Used only when total is a multiple of 8.
 __device__ inline uint32_t xcd_remap(uint32_t bid, uint32_t total) {

@@ -179,39 +179,17 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
   }
 }
 
-// One wave per (batch·head, query): lane t owns output columns t, t + 64, ...  The chunk statistics
-// are the same for every lane of the wave.
+// One wave per (batch·head, query): merge_partials over the query's S chunks.
 template <int D>
 __global__ __launch_bounds__(64) void decode_merge_kernel(const float* __restrict__ part_o,
                                                           const float* __restrict__ part_ml,
                                                           bf16* __restrict__ O,
                                                           float* __restrict__ LSE, int Nq, int S) {
-  constexpr int PER = (D + 63) / 64;  // values per lane (the last partly idle when D = 96)
-  const int lane = threadIdx.x;
   const int bh = blockIdx.x / Nq;
   const int qi = blockIdx.x % Nq;
-  const size_t row0 = (size_t)bh * S * Nq + qi;  // chunk s: row0 + s·Nq
-  float m = -INFINITY;
-  for (int s = 0; s < S; ++s) m = fmaxf(m, part_ml[3 * (row0 + (size_t)s * Nq)]);
-  float l = 0.f, lr = 0.f, acc[PER];
-#pragma unroll
-  for (int t = 0; t < PER; ++t) acc[t] = 0.f;
-  for (int s = 0; s < S; ++s) {
-    const size_t row = row0 + (size_t)s * Nq;
-    const float ms = part_ml[3 * row];
-    const float w = exp2_fast(ms - m);  // 0 for a chunk without usable keys (ms = -inf)
-    l += w * part_ml[3 * row + 1];
-    lr += w * part_ml[3 * row + 2];
-#pragma unroll
-    for (int t = 0; t < PER; ++t)
-      if (D % 64 == 0 || lane + 64 * t < D) acc[t] += w * part_o[row * D + lane + 64 * t];
-  }
-  const float inv = 1.f / lr;
-  const size_t orow = ((size_t)bh * Nq + qi) * D;
-#pragma unroll
-  for (int t = 0; t < PER; ++t)
-    if (D % 64 == 0 || lane + 64 * t < D) O[orow + lane + 64 * t] = (__bf16)(acc[t] * inv);
-  if (lane == 0) LSE[(size_t)bh * Nq + qi] = (m + __log2f(l)) * kLn2;
+  const size_t out_row = (size_t)bh * Nq + qi;
+  merge_partials<D>(part_o, part_ml, (size_t)bh * S * Nq + qi, (size_t)Nq, S, O + out_row * D,
+                    LSE + out_row, threadIdx.x);
 }
 
 template <int D, bool CAUSAL>

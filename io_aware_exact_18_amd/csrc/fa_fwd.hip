@@ -79,10 +79,19 @@ __device__ inline void scores_tile(const char* klds, const FragOffsets<lds_cols<
   for (int i = 0; i < 2 * NS; ++i) acc[i & 1] = mfma_32x32x16(f[i], qf[i >> 1], acc[i & 1]);
 }
 
-template <int D, bool CAUSAL>
+// Partial-result outputs of the key-range split (fwd_split in fa_launch.h).
+struct SplitOut {
+  float* part_o;   // [nseg][B·H][N][D]: unnormalised output of the segment's keys
+  float* part_ml;  // [nseg][B·H][N][3]: reference maximum (base 2), fp32 and bf16-rounded row sums
+  int seg;         // key tiles per segment
+  int bh_count;    // B·H
+};
+
+template <int D, bool CAUSAL, bool SPLIT>
 __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
-    bf16* __restrict__ O, float* __restrict__ LSE, int N, int nqt, float scale_log2, int remap) {
+    bf16* __restrict__ O, float* __restrict__ LSE, int N, int nqt, float scale_log2, int remap,
+    SplitOut so) {
   static_assert(D <= 128, "head dimension 256 runs fwd_bf16_split_kernel");
   constexpr int KSTEPS = D / 16;  // k-steps of the Sᵀ product
   constexpr int DB = D / 32;      // 32-row blocks of Oᵀ
@@ -102,7 +111,13 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
   const int lc = lane & 31;  // row / column index inside a 32-wide matrix-core tile
 
   const uint32_t total = gridDim.x;
-  const uint32_t logical = remap ? xcd_remap(blockIdx.x, total) : blockIdx.x;
+  uint32_t logical = remap ? xcd_remap(blockIdx.x, total) : blockIdx.x;
+  int sg = 0;  // key segment (split only): work items are segment-major
+  if constexpr (SPLIT) {
+    const uint32_t per_seg = (uint32_t)so.bh_count * (uint32_t)nqt;
+    sg = (int)(logical / per_seg);
+    logical %= per_seg;
+  }
   const int bh = logical / nqt;
   int qt = logical % nqt;
   if (CAUSAL) qt = nqt - 1 - qt;
@@ -125,14 +140,18 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
 
   const int kv_end = CAUSAL ? min(N, q0 + kBR) : N;
   const int ntiles = (kv_end + kBC - 1) / kBC;
+  // Key tiles [t_beg, t_end) of this workgroup: all of them, or one segment of the split.
+  const int t_beg = SPLIT ? sg * so.seg : 0;
+  const int t_end = SPLIT ? min(ntiles, t_beg + so.seg) : ntiles;
+  if (SPLIT && t_beg >= t_end) return;  // the query tile's keys end before this segment
   // Tiles at or beyond this index are fully masked for this wave (causal): no math on them.
-  const int wave_tiles = CAUSAL ? min(ntiles, (qw + 31) / kBC + 1) : ntiles;
+  const int wave_tiles = CAUSAL ? min(t_end, (qw + 31) / kBC + 1) : t_end;
   const FragOffsets<L> fo(lane);
 
-  // Prologue: K(0), K(1), V(0) in flight; scores of tile 0.
-  copy(mk, 0, k0s);
-  if (ntiles > 1) copy(mk, kBC, k1s);
-  copy(mv, 0, v0s);
+  // Prologue: K(t_beg), K(t_beg + 1), V(t_beg) in flight; scores of tile t_beg.
+  copy(mk, t_beg * kBC, k0s);
+  if (t_beg + 1 < t_end) copy(mk, (t_beg + 1) * kBC, k1s);
+  copy(mv, t_beg * kBC, v0s);
   wait_vmem_all();
   __syncthreads();
 
@@ -160,8 +179,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[b][r] = 0.f;
 
-  // One tile; P is the parity of j, a compile-time constant so every LDS address below is a lane
-  // base plus an immediate.  Buffers on entry: k[P^1] = K(j+1), v[P] = V(j); k[P], v[P^1] are free.
+  // One tile; P is the parity of j − t_beg, a compile-time constant so every LDS address below is a
+  // lane base plus an immediate.  Buffers on entry: k[P^1] = K(j+1), v[P] = V(j); k[P], v[P^1] are free.
   auto tile = [&](auto parity, int j) {
     constexpr int P = decltype(parity)::value;
     f32x16(&s_cur)[2] = pick<P>(sa, sb);  // scores of tile j
@@ -170,8 +189,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     bf16* const k_next = P ? k0s : k1s;   // holds K(j+1)
     bf16* const v_this = P ? v1s : v0s;   // holds V(j)
     bf16* const v_next = P ? v0s : v1s;   // free: receives V(j+1)
-    if (j + 2 < ntiles) copy(mk, (j + 2) * kBC, k_this);
-    if (j + 1 < ntiles) copy(mv, (j + 1) * kBC, v_next);
+    if (j + 2 < t_end) copy(mk, (j + 2) * kBC, k_this);
+    if (j + 1 < t_end) copy(mv, (j + 1) * kBC, v_next);
     const int kv0 = j * kBC;
     if (j < wave_tiles) {
       // Accumulator element (kb, r) is key kv0 + 32kb + 8(r/4) + 4g + (r%4) for query qi.  Diagonal
@@ -257,9 +276,34 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     __syncthreads();
   };
 
-  for (int j = 0; j < ntiles; j += 2) {
+  for (int j = t_beg; j < t_end; j += 2) {
     tile(std::integral_constant<int, 0>{}, j);
-    if (j + 1 < ntiles) tile(std::integral_constant<int, 1>{}, j + 1);
+    if (j + 1 < t_end) tile(std::integral_constant<int, 1>{}, j + 1);
+  }
+
+  if constexpr (SPLIT) {
+    // The segment's partial result: unnormalised Oᵀ column, reference maximum and both row sums (a
+    // wave without keys in the segment writes m = −inf and zeros, which the merge weighs by 0).
+    const float l_seg = halves_sum(l);
+    const float lr_seg = halves_sum(lr);
+    if (qi < N) {
+      const size_t row = ((size_t)sg * so.bh_count + bh) * N + qi;
+      float* orow = so.part_o + row * D;
+#pragma unroll
+      for (int b = 0; b < DB; ++b)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const f32x4 w = {oacc[b][4 * r4], oacc[b][4 * r4 + 1], oacc[b][4 * r4 + 2],
+                           oacc[b][4 * r4 + 3]};
+          *(f32x4*)&orow[32 * b + 8 * r4 + 4 * g] = w;
+        }
+      if (g == 0) {
+        so.part_ml[3 * row] = m;
+        so.part_ml[3 * row + 1] = l_seg;
+        so.part_ml[3 * row + 2] = lr_seg;
+      }
+    }
+    return;
   }
 
   // Epilogue: combine the two half-row sums, normalise by the rounded weights' sum, write O and LSE.
@@ -478,15 +522,50 @@ hipError_t launch_split(const FwdArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// Key-range split: one wave per (batch·head, query) combines the row's segments (as many as its
+// query tile's key range spans).
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(64) void fwd_merge_kernel(const float* __restrict__ part_o,
+                                                       const float* __restrict__ part_ml,
+                                                       bf16* __restrict__ O, float* __restrict__ LSE,
+                                                       int N, int bh_count, int seg) {
+  const size_t r = blockIdx.x;  // output row (batch·head, query)
+  const int bh = (int)(r / (size_t)N);
+  const int qi = (int)(r % (size_t)N);
+  const int kv_end = CAUSAL ? min(N, (qi / kBR + 1) * kBR) : N;
+  const int nseg = ((kv_end + kBC - 1) / kBC + seg - 1) / seg;
+  merge_partials<D>(part_o, part_ml, (size_t)bh * N + qi, (size_t)bh_count * N, nseg, O + r * D,
+                    LSE + r, threadIdx.x);
+}
+
 template <int D, bool CAUSAL>
 hipError_t launch(const FwdArgs& a, hipStream_t stream) {
   const int nqt = (a.N + kBR - 1) / kBR;
-  const uint32_t total = (uint32_t)a.B * a.H * nqt;
-  const int remap = use_xcd_order(total, (long)a.B * a.H, CAUSAL ? 1 : 0);
   const float scale_log2 = a.scale * kLog2e;
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL>), dim3(total), dim3(kThreads), 0, stream,
+  const uint32_t bh = (uint32_t)a.B * a.H;
+  const FwdSplit sp = a.workspace ? fwd_split(a.B, a.H, a.N, D, CAUSAL ? 1 : 0) : FwdSplit{0, 1};
+  if (sp.nseg > 1) {
+    // Segment-major work items dealt round-robin to the XCDs (remap off): segments of one key range
+    // cost about the same, and the round-robin spreads the empty items (segments past a query tile's
+    // keys, which return at once) evenly.
+    SplitOut so{(float*)a.workspace, nullptr, sp.seg, (int)bh};
+    so.part_ml = so.part_o + (size_t)sp.nseg * bh * a.N * D;
+    const uint32_t total = (uint32_t)sp.nseg * bh * nqt;
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, true>), dim3(total), dim3(kThreads), 0, stream,
+                       (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, (bf16*)a.o, a.lse, a.N,
+                       nqt, scale_log2, 0, so);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((fwd_merge_kernel<D, CAUSAL>), dim3(bh * (uint32_t)a.N), dim3(64), 0, stream,
+                       (const float*)so.part_o, (const float*)so.part_ml, (bf16*)a.o, a.lse, a.N,
+                       (int)bh, sp.seg);
+    return hipGetLastError();
+  }
+  const uint32_t total = bh * nqt;
+  const int remap = use_xcd_order(total, (long)bh, CAUSAL ? 1 : 0);
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, false>), dim3(total), dim3(kThreads), 0, stream,
                      (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, (bf16*)a.o, a.lse, a.N,
-                     nqt, scale_log2, remap);
+                     nqt, scale_log2, remap, SplitOut{nullptr, nullptr, 0, 0});
   return hipGetLastError();
 }
 

@@ -14,6 +14,7 @@ struct FwdArgs {
   float* lse;
   int B, H, N, d, causal;
   float scale;
+  void* workspace = nullptr;  // fwd_split_workspace_bytes bytes: allows the key-range split
 };
 
 struct Fp8FwdArgs {
@@ -96,6 +97,53 @@ inline DecodeSplit decode_split(int B, int H, int Nq, int Nk) {
 inline size_t decode_workspace_bytes(int B, int H, int Nq, int Nk, int d) {
   const DecodeSplit sp = decode_split(B, H, Nq, Nk);
   return (((size_t)B * H * sp.S * Nq * ((size_t)d + 3) * sizeof(float)) + 255u) & ~(size_t)255u;
+}
+
+// Key-range split of the bf16 forward, for grids too small to fill the device (few heads, long
+// sequences): every 128-query tile's key tiles are cut into segments of `seg` 64-key tiles, each
+// (query tile, segment) pair is one workgroup writing a partial result, and a merge kernel combines a
+// row's segments.  nseg = 1 means no split.
+// Rule (measured on MI355X, causal d = 128, 1–8 heads of 4k–64k keys): with T the key tiles summed
+// over all (batch·head, query tile) pairs and kt = ⌈N/64⌉ the longest range, the unsplit grid leaves
+// compute units idle when kt exceeds the average work per workgroup slot, T / kSlots (two workgroups
+// on each of the 256 compute units).  The split is used when kt ≥ 4·T/kSlots, or when kt ≥ 1.5·T/kSlots
+// and rows are long (kt ≥ 256 tiles); below that, the partial results' traffic (d + 3 fp32 values
+// per row and segment, written and read back) and the shorter workgroups cost more than the balance
+// gains (2×4×8192: 739 TFLOP/s unsplit, 564–656 split).  Segments of kt/8 tiles, clamped to 16..128,
+// were within 6% of the best segment length for every shape measured (1×1×16384: 261 → 526 TFLOP/s;
+// 1×1×65536: 861 → 1011).  Head dimension 256 (its own kernel) is not split.
+constexpr long kSlots = 512;
+struct FwdSplit {
+  int seg;   // key tiles per segment
+  int nseg;  // segments of the longest key range
+};
+inline FwdSplit fwd_split(int B, int H, int N, int d, int causal) {
+  FwdSplit r{0, 1};
+  if (d > 128) return r;
+  const long bh = (long)B * H;
+  const long nqt = ((long)N + 127) / 128;
+  const long kt = ((long)N + 63) / 64;
+  long total = 0;  // key tiles over every (batch·head, query tile)
+  for (long qt = 0; qt < nqt; ++qt) {
+    const long end = causal ? ((qt + 1) * 128 < (long)N ? (qt + 1) * 128 : (long)N) : (long)N;
+    total += (end + 63) / 64;
+  }
+  total *= bh;
+  if (2 * kt * kSlots < 3 * total) return r;
+  if (kt * kSlots < 4 * total && kt < 256) return r;
+  long seg = kt / 8;
+  seg = seg < 16 ? 16 : (seg > 128 ? 128 : seg);
+  if (seg >= kt) return r;
+  r.seg = (int)seg;
+  r.nseg = (int)((kt + seg - 1) / seg);
+  return r;
+}
+// Workspace of fa_fwd_split: per (segment, batch·head, query) the unnormalised output (d fp32) and the
+// segment's reference maximum and two row sums (3 fp32), rounded up to 256 bytes; 0 without a split.
+inline size_t fwd_split_workspace_bytes(int B, int H, int N, int d, int causal) {
+  const FwdSplit sp = fwd_split(B, H, N, d, causal);
+  if (sp.nseg <= 1) return 0;
+  return (((size_t)sp.nseg * B * H * N * ((size_t)d + 3) * sizeof(float)) + 255u) & ~(size_t)255u;
 }
 
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream);

@@ -23,6 +23,9 @@ def lib():
     lib = ctypes.CDLL(LIB)
     vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, vp]
+    lib.fa_fwd_split_workspace_bytes.argtypes = [i, i, i, i, i]
+    lib.fa_fwd_split_workspace_bytes.restype = sz
+    lib.fa_fwd_split.argtypes = [vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, f, vp]
     lib.fa_fwd_fp8.argtypes = [vp, vp, vp, f, f, f, vp, vp, i, i, i, i, i, f, vp]
     lib.fa_bwd_workspace_bytes.argtypes = [i, i, i, i]
     lib.fa_bwd_workspace_bytes.restype = sz
@@ -45,7 +48,7 @@ def lib():
 def test_exports_match_header(lib):
     text = open(HEADER).read()
     declared = set(re.findall(r"^\s*(?:fa_status|size_t|const char\*)\s+(fa_\w+)\s*\(", text, re.M))
-    assert declared == {"fa_fwd", "fa_fwd_fp8", "fa_bwd_workspace_bytes", "fa_bwd", "fa_status_str",
+    assert declared == {"fa_fwd", "fa_fwd_split", "fa_fwd_split_workspace_bytes", "fa_fwd_fp8", "fa_bwd_workspace_bytes", "fa_bwd", "fa_status_str",
                         "fa_bwd_preprocess", "fa_bwd_dkdv", "fa_bwd_dq", "fa_device_info",
                         "fa_decode", "fa_decode_workspace_bytes", "fa_bwd_fp8",
                         "fa_bwd_fp8_workspace_bytes", "fa_bwd_noalloc", "fa_bwd_noalloc_max_rows",
@@ -93,6 +96,59 @@ def test_fwd_rejections(lib):
 
 def fwd8(lib, d=128, qs=1.0, ks=1.0, vs=1.0, k8=P, scale=0.09):
     return lib.fa_fwd_fp8(P, k8, P, qs, ks, vs, P, P, 1, 1, 64, d, 1, scale, None)
+
+
+def _fwd_split(B, H, N, d, causal):
+    """The split rule fa.h documents for fa_fwd_split: (seg, nseg), nseg = 1 when not split."""
+    nqt, kt = -(-N // 128), -(-N // 64)
+    total = B * H * sum(-(-(min(N, (qt + 1) * 128) if causal else N) // 64) for qt in range(nqt))
+    if d > 128 or 2 * kt * 512 < 3 * total or (kt * 512 < 4 * total and kt < 256):
+        return 0, 1
+    seg = min(128, max(16, kt // 8))
+    return (0, 1) if seg >= kt else (seg, -(-kt // seg))
+
+
+def test_fwd_split_workspace_formula(lib):
+    cases = ((1, 1, 16384, 128, 1), (1, 1, 65536, 128, 1), (1, 4, 32768, 64, 1), (1, 1, 4097, 96, 0),
+             (2, 3, 5000, 128, 1), (1, 1, 1024, 64, 1), (1, 1, 1025, 64, 0), (4, 32, 4096, 128, 1),
+             (1, 32, 16384, 128, 1), (8, 16, 2048, 64, 0), (1, 1, 65536, 256, 1), (2, 4, 8192, 128, 1),
+             (2, 2, 16384, 128, 1), (1, 8, 16384, 128, 1), (1, 2, 8192, 128, 1), (1, 1, 1 << 20, 128, 1))
+    split_seen = 0
+    for B, H, N, d, causal in cases:
+        seg, nseg = _fwd_split(B, H, N, d, causal)
+        want = 0 if nseg == 1 else -(-(nseg * B * H * N * (d + 3) * 4) // 256) * 256
+        assert lib.fa_fwd_split_workspace_bytes(B, H, N, d, causal) == want, (B, H, N, d, causal)
+        if nseg > 1:
+            split_seen += 1
+            assert (nseg - 1) * seg < -(-N // 64) <= nseg * seg
+    assert split_seen >= 5
+    # measured choices: short grids of long rows split, full grids and head dimension 256 never
+    for shape in ((1, 1, 16384, 128, 1), (1, 1, 65536, 128, 1), (2, 2, 16384, 128, 1)):
+        assert lib.fa_fwd_split_workspace_bytes(*shape) > 0, shape
+    for shape in ((4, 32, 4096, 128, 1), (2, 4, 8192, 128, 1), (1, 8, 16384, 128, 1),
+                  (1, 32, 16384, 128, 1), (8, 16, 2048, 64, 0), (1, 1, 65536, 256, 1)):
+        assert lib.fa_fwd_split_workspace_bytes(*shape) == 0, shape
+    for bad in ((0, 1, 8, 64, 1), (1, 1, 0, 64, 1), (1, 1, 8, 80, 1), (1, 1, 1 << 23, 128, 1)):
+        assert lib.fa_fwd_split_workspace_bytes(*bad) == 0, bad
+
+
+def fwd_split(lib, q=P, k=P, v=P, o=P, lse=P, ws=P, ws_bytes=1 << 34, B=1, H=1, N=16384, d=128,
+              causal=1, scale=0.125):
+    return lib.fa_fwd_split(q, k, v, o, lse, ws, ws_bytes, B, H, N, d, causal, scale, None)
+
+
+def test_fwd_split_rejections(lib):
+    assert fwd_split(lib, q=None) == NULL
+    assert fwd_split(lib, lse=None) == NULL
+    assert fwd_split(lib, N=0) == SHAPE
+    assert fwd_split(lib, d=80) == UNSUP
+    assert fwd_split(lib, scale=-1.0) == UNSUP
+    assert fwd_split(lib, o=MIS) == ALIGN
+    need = lib.fa_fwd_split_workspace_bytes(1, 1, 16384, 128, 1)
+    assert need > 0
+    assert fwd_split(lib, ws=None) == WORKSPACE
+    assert fwd_split(lib, ws_bytes=need - 1) == WORKSPACE
+    assert fwd_split(lib, ws=P + 16) == ALIGN
 
 
 def test_fwd_fp8_rejections(lib):
