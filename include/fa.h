@@ -153,6 +153,29 @@ fa_status fa_bwd_delta_dq(const void* q, const void* k, const void* v, const voi
                           float softmax_scale, hipStream_t stream);
 
 /*
+ * Backward pass as fa_bwd, with a workspace that lets the library split the loops of both backward
+ * kernels for the same shapes fa_fwd_split splits (few heads, long sequences).  The dQ kernel splits
+ * each 128-query tile's key range into fa_fwd_split's segments of seg 64-key tiles; the dK/dV kernel
+ * splits each 128-key block's query range into segments of 2·seg 32-query steps.  Each segment writes
+ * fp32 partial sums of its gradients to the workspace and a last kernel adds a row's segments, applies
+ * the scale and rounds to bf16 (the gradients of "Anatomy of a FlashAttention Kernel", section "How
+ * does FlashAttention save memory in the backward pass?", summed over key or query ranges in another
+ * grouping).  Results can differ from fa_bwd's in the last bits.
+ *   workspace  at least fa_bwd_split_workspace_bytes(B, H, N, d, causal) bytes, 256-byte aligned,
+ *              owned by the caller, contents undefined after the call: −D_i (as fa_bwd), then, when
+ *              split, nseg_q·B·H·N·d fp32 partial dQ sums and nseg_k·B·H·N·d each for dK and dV,
+ *              each array rounded up to 256 bytes, with nseg_q = fa_fwd_split's nseg and nseg_k =
+ *              ⌈⌈N/32⌉ / (2·seg)⌉.  Without a split the size is fa_bwd_workspace_bytes and the call is
+ *              fa_bwd.
+ * Errors: as fa_bwd.
+ */
+size_t fa_bwd_split_workspace_bytes(int B, int H, int N, int d, int causal);
+fa_status fa_bwd_split(const void* q, const void* k, const void* v, const void* o,
+                       const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                       void* workspace, size_t workspace_bytes, int B, int H, int N, int d,
+                       int causal, float softmax_scale, hipStream_t stream);
+
+/*
  * Backward pass of the FP8 forward (fa_fwd_fp8): the gradients of O = softmax(scale · Q Kᵀ) V with
  * respect to the dequantised inputs Q = q8 · q_descale, K = k8 · k_descale, V = v8 · v_descale
  * ("Anatomy ...", sections "How does FlashAttention save memory in the backward pass?" and "What

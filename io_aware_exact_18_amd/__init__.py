@@ -27,7 +27,8 @@ import os
 
 import torch
 
-__all__ = ["fwd", "fwd_split", "fwd_split_workspace_bytes", "fwd_fp8", "bwd", "bwd_workspace_bytes", "bwd_preprocess", "bwd_dkdv",
+__all__ = ["fwd", "fwd_split", "fwd_split_workspace_bytes", "fwd_fp8", "bwd", "bwd_split",
+           "bwd_split_workspace_bytes", "bwd_workspace_bytes", "bwd_preprocess", "bwd_dkdv",
            "bwd_dq", "bwd_delta_dq", "bwd_fp8", "bwd_fp8_workspace_bytes", "decode",
            "decode_workspace_bytes",
            "status_str", "device_info", "FaError", "library", "LIB_PATH"]
@@ -70,6 +71,11 @@ def library():
         lib.fa_bwd_workspace_bytes.restype = sz
         lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, f, vp]
         lib.fa_bwd.restype = i
+        lib.fa_bwd_split_workspace_bytes.argtypes = [i, i, i, i, i]
+        lib.fa_bwd_split_workspace_bytes.restype = sz
+        lib.fa_bwd_split.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, f,
+                                     vp]
+        lib.fa_bwd_split.restype = i
         lib.fa_bwd_preprocess.argtypes = [vp, vp, vp, sz, i, i, i, i, vp]
         lib.fa_bwd_preprocess.restype = i
         lib.fa_bwd_dkdv.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, f, vp]
@@ -264,6 +270,36 @@ def bwd(q, k, v, o, lse, dout, causal, scale=None, workspace=None):
                                 dv.data_ptr(), workspace.data_ptr(), workspace.numel(), B, H, N, d,
                                 int(bool(causal)), _scale(scale, d), _stream(q.device))
     _check("fa_bwd", code)
+    return dq, dk, dv
+
+
+def bwd_split_workspace_bytes(B, H, N, d, causal):
+    """Bytes of workspace fa_bwd_split needs (fa_bwd's when the shape is not split; 0 if rejected)."""
+    return int(library().fa_bwd_split_workspace_bytes(B, H, N, d, int(bool(causal))))
+
+
+def bwd_split(q, k, v, o, lse, dout, causal, scale=None, workspace=None):
+    """Backward pass that may split the backward kernels' loops (fa_bwd_split): returns (dq, dk, dv)
+    as bwd.  The workspace (uint8, device) is allocated here when not given."""
+    _require(q, "q", torch.bfloat16)
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, N, d]")
+    for t, name in ((k, "k"), (v, "v"), (o, "o"), (dout, "dout")):
+        _require(t, name, torch.bfloat16, q.shape, device=q.device)
+    B, H, N, d = q.shape
+    _require(lse, "lse", torch.float32, (B, H, N), device=q.device)
+    if workspace is None:
+        workspace = torch.empty(max(bwd_split_workspace_bytes(B, H, N, d, causal), 1),
+                                dtype=torch.uint8, device=q.device)
+    else:
+        _require(workspace, "workspace", torch.uint8, device=q.device)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    with torch.cuda.device(q.device):
+        code = library().fa_bwd_split(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                      lse.data_ptr(), dout.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                                      dv.data_ptr(), workspace.data_ptr(), workspace.numel(), B, H,
+                                      N, d, int(bool(causal)), _scale(scale, d), _stream(q.device))
+    _check("fa_bwd_split", code)
     return dq, dk, dv
 
 

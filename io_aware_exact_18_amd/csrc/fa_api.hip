@@ -280,6 +280,47 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
   return fa::launch_bwd(a, stream) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
+size_t fa_bwd_split_workspace_bytes(int B, int H, int N, int d, int causal) {
+  if (check_shape(B, H, N, d, 2) != FA_OK) return 0;
+  return fa::bwd_split_workspace_bytes(B, H, N, d, causal ? 1 : 0);
+}
+
+fa_status fa_bwd_split(const void* q, const void* k, const void* v, const void* o,
+                       const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                       void* workspace, size_t workspace_bytes, int B, int H, int N, int d,
+                       int causal, float softmax_scale, hipStream_t stream) {
+  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return FA_ERR_NULL;
+  fa::BwdArgs a{};
+  const void* ptrs[] = {q, k, v, o, lse, dout, dq, dk, dv};
+  fa_status st = check_bwd(ptrs, 9, workspace, workspace_bytes, B, H, N, d, &a);
+  if (st != FA_OK) return st;
+  if (!good_scale(softmax_scale)) return FA_ERR_UNSUPPORTED;
+  if (workspace_bytes < fa::bwd_split_workspace_bytes(B, H, N, d, causal ? 1 : 0))
+    return FA_ERR_WORKSPACE;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.dout = dout;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.causal = causal ? 1 : 0;
+  a.scale = a.dk_scale = a.dq_scale = softmax_scale;
+  const fa::BwdSplit sp = fa::bwd_split(B, H, N, d, a.causal);
+  if (sp.seg > 0) {  // partial sums after D: dQ's, then dK's and dV's
+    char* p = (char*)workspace + fa::bwd_delta_bytes(B, H, N);
+    a.split_seg = sp.seg;
+    a.part_dq = (float*)p;
+    p += fa::bwd_split_part_bytes(sp.nseg_q, B, H, N, d);
+    a.part_dk = (float*)p;
+    p += fa::bwd_split_part_bytes(sp.nseg_k, B, H, N, d);
+    a.part_dv = (float*)p;
+  }
+  return fa::launch_bwd(a, stream) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
 size_t fa_bwd_fp8_workspace_bytes(int B, int H, int N, int d) {
   if (check_shape(B, H, N, d, 2) != FA_OK) return 0;
   return fa::bwd_fp8_workspace_bytes(B, H, N, d);

@@ -81,12 +81,22 @@ __global__ __launch_bounds__(kThreads) void bwd_pre_kernel(const bf16* __restric
 // (dV, then dK): with both, the dKᵀ and dVᵀ accumulators alone would take all of a wave's 512
 // registers' worth of room it needs for the K fragments and the step's tiles; the dV pass needs
 // neither V nor dP, and the extra cost is one more S product per step.
-template <int D, bool CAUSAL, int OUT>
+// Partial-result outputs of the split backward (bwd_split in fa_launch.h): fp32 [nseg][B·H][N][D]
+// arrays of unscaled gradient sums, one per segment of the workgroup's loop.
+struct BwdSplitOut {
+  float* part_a;  // dK/dV kernel: dKᵀ sums; dQ kernel: dQᵀ sums
+  float* part_b;  // dK/dV kernel: dVᵀ sums
+  int seg;        // loop steps (dK/dV: 32-query steps; dQ: 64-key tiles) per segment
+  int bh_count;   // B·H
+};
+
+template <int D, bool CAUSAL, int OUT, bool SPLIT>
 __global__ __launch_bounds__(kThreads, (D == 256 && OUT != 1) ? 1 : 2) void bwd_dkdv_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     const float* __restrict__ LSE, const bf16* __restrict__ dO, const float* __restrict__ Delta,
     bf16* __restrict__ dK, bf16* __restrict__ dV, int N, int nkt, float scale, float scale_log2,
-    int remap) {
+    int remap, BwdSplitOut so) {
+  static_assert(!SPLIT || OUT == 3, "the split backward runs the fused dK/dV kernel");
   constexpr int KSTEPS = D / 16;
   constexpr int DB = D / 32;
   constexpr int L = lds_cols<D>();
@@ -111,12 +121,25 @@ __global__ __launch_bounds__(kThreads, (D == 256 && OUT != 1) ? 1 : 2) void bwd_
   const int g = lane >> 5;
   const int lc = lane & 31;
 
-  const uint32_t logical = remap ? xcd_remap(blockIdx.x, gridDim.x) : blockIdx.x;
+  uint32_t logical = remap ? xcd_remap(blockIdx.x, gridDim.x) : blockIdx.x;
+  int sg = 0;  // segment of the query steps (split only): work items are segment-major
+  if constexpr (SPLIT) {
+    const uint32_t per_seg = (uint32_t)so.bh_count * (uint32_t)nkt;
+    sg = (int)(logical / per_seg);
+    logical %= per_seg;
+  }
   const int bh = logical / nkt;
   const int kt = logical % nkt;
   const int k0 = kt * kBKV;
   const int kw = k0 + 32 * wave;  // first key of this wave
   const int kj = kw + lc;         // this lane's key (column of the score tiles)
+
+  const int qstart = CAUSAL ? k0 : 0;  // causal: only queries ≥ the tile's first key
+  const int nsteps = (N - qstart + kBQ - 1) / kBQ;
+  // Steps [s_beg, s_end) of this workgroup: all of them, or one segment of the split.
+  const int s_beg = SPLIT ? sg * so.seg : 0;
+  const int s_end = SPLIT ? min(nsteps, s_beg + so.seg) : nsteps;
+  if (SPLIT && s_beg >= s_end) return;  // the key block's queries end before this segment
 
   const size_t head = (size_t)bh * N * D;
   const uint32_t head_bytes = (uint32_t)N * D * 2u;
@@ -140,8 +163,6 @@ __global__ __launch_bounds__(kThreads, (D == 256 && OUT != 1) ? 1 : 2) void bwd_
   }
 
   const FragOffsets<L> fo(lane);
-  const int qstart = CAUSAL ? k0 : 0;  // causal: only queries ≥ the tile's first key
-  const int nsteps = (N - qstart + kBQ - 1) / kBQ;
   // Query tiles are walked from the last one down to qstart: every workgroup of a head starts on the
   // same tiles and they move through Q and dO together, so each tile is read from memory about once
   // and then served from L2 to the head's other key blocks (ascending, the key blocks would start at
@@ -169,20 +190,20 @@ __global__ __launch_bounds__(kThreads, (D == 256 && OUT != 1) ? 1 : 2) void bwd_
       dva[b][r] = 0.f;
     }
 
-  stage(0, q0s, o0s, d0s);
+  stage(s_beg, q0s, o0s, d0s);
   wait_vmem_all();
   if (wave == 0) l0s[lane] = lse_next * kLog2e;
   __syncthreads();
 
-  // One query tile; P (the step's parity) is a compile-time constant so the buffers are fixed
-  // objects.  On entry the tile is in buffer P; buffer P^1 is free and receives the next tile.
+  // One query tile; P (the parity of step − s_beg) is a compile-time constant so the buffers are
+  // fixed objects.  On entry the tile is in buffer P; buffer P^1 is free and receives the next tile.
   auto step_fn = [&](auto parity, int step) {
     constexpr int P = decltype(parity)::value;
     const char* qs = (const char*)(P ? q1s : q0s);
     const char* dos = (const char*)(P ? o1s : o0s);
     const float* lse_s = P ? l1s : l0s;
     const float* del_s = P ? d1s : d0s;
-    if (step + 1 < nsteps) stage(step + 1, P ? q0s : q1s, P ? o0s : o1s, P ? d0s : d1s);
+    if (step + 1 < s_end) stage(step + 1, P ? q0s : q1s, P ? o0s : o1s, P ? d0s : d1s);
     const int qb = step_q(step);
 
     if (!(CAUSAL && kw > qb + kBQ - 1)) {  // every (query, key) pair masked for this wave: skip
@@ -244,13 +265,32 @@ __global__ __launch_bounds__(kThreads, (D == 256 && OUT != 1) ? 1 : 2) void bwd_
       }
     }
     wait_vmem_all();
-    if (wave == 0 && step + 1 < nsteps) (P ? l0s : l1s)[lane] = lse_next * kLog2e;
+    if (wave == 0 && step + 1 < s_end) (P ? l0s : l1s)[lane] = lse_next * kLog2e;
     __syncthreads();
   };
 
-  for (int step = 0; step < nsteps; step += 2) {
+  for (int step = s_beg; step < s_end; step += 2) {
     step_fn(std::integral_constant<int, 0>{}, step);
-    if (step + 1 < nsteps) step_fn(std::integral_constant<int, 1>{}, step + 1);
+    if (step + 1 < s_end) step_fn(std::integral_constant<int, 1>{}, step + 1);
+  }
+
+  if constexpr (SPLIT) {
+    // The segment's unscaled dKᵀ and dVᵀ sums for this lane's key (d rows 32b + 8(r/4) + 4g + 0..3).
+    if (kj < N) {
+      const size_t row = ((size_t)sg * so.bh_count + bh) * N + kj;
+      float* kr = so.part_a + row * D;
+      float* vr = so.part_b + row * D;
+#pragma unroll
+      for (int b = 0; b < DB; ++b)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          *(f32x4*)&kr[32 * b + 8 * r4 + 4 * g] = f32x4{dka[b][4 * r4], dka[b][4 * r4 + 1],
+                                                        dka[b][4 * r4 + 2], dka[b][4 * r4 + 3]};
+          *(f32x4*)&vr[32 * b + 8 * r4 + 4 * g] = f32x4{dva[b][4 * r4], dva[b][4 * r4 + 1],
+                                                        dva[b][4 * r4 + 2], dva[b][4 * r4 + 3]};
+        }
+    }
+    return;
   }
 
   // Epilogue: dK = scale · (dKᵀ)ᵀ, dV = (dVᵀ)ᵀ; this lane owns key kj, d rows 32b + 8(r/4) + 4g + (0..3).
@@ -285,12 +325,12 @@ __global__ __launch_bounds__(kThreads, (D == 256 && OUT != 1) ? 1 : 2) void bwd_
 // thread t of a row sums d values 8t .. 8t + 7, here chunk (s, g) of lane (query, g), t = 2s + g, so its
 // tree levels t ^ 2h are in-lane (s ^ h) and t ^ 1 is the other half-wave.  Head dimension 96 (runs of
 // 24 values per bwd_pre thread, which straddle the half-waves) keeps the separate launch.
-template <int D, bool CAUSAL, bool WITH_D>
+template <int D, bool CAUSAL, bool WITH_D, bool SPLIT>
 __global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void bwd_dq_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     const float* __restrict__ LSE, const bf16* __restrict__ dO, float* __restrict__ Delta,
     const bf16* __restrict__ O, bf16* __restrict__ dQ, int N, int nqt, float scale,
-    float scale_log2, float delta_mult, int remap) {
+    float scale_log2, float delta_mult, int remap, BwdSplitOut so) {
   static_assert(!WITH_D || pre_tpr<D>() == D / 8, "D in the dQ kernel: runs of 8 values");
   constexpr int KSTEPS = D / 16;
   constexpr int DB = D / 32;
@@ -308,13 +348,26 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void bwd_dq_kernel(
   const int g = lane >> 5;
   const int lc = lane & 31;
 
-  const uint32_t logical = remap ? xcd_remap(blockIdx.x, gridDim.x) : blockIdx.x;
+  uint32_t logical = remap ? xcd_remap(blockIdx.x, gridDim.x) : blockIdx.x;
+  int sg = 0;  // key segment (split only): work items are segment-major
+  if constexpr (SPLIT) {
+    const uint32_t per_seg = (uint32_t)so.bh_count * (uint32_t)nqt;
+    sg = (int)(logical / per_seg);
+    logical %= per_seg;
+  }
   const int bh = logical / nqt;
   int qt = logical % nqt;
   if (CAUSAL) qt = nqt - 1 - qt;  // heaviest tiles first
   const int q0 = qt * kBR;
   const int qw = q0 + 32 * wave;
   const int qi = qw + lc;  // this lane's query
+
+  const int kv_end = CAUSAL ? min(N, q0 + kBR) : N;
+  const int ntiles = (kv_end + kBC - 1) / kBC;
+  // Key tiles [t_beg, t_end) of this workgroup: all of them, or one segment of the split.
+  const int t_beg = SPLIT ? sg * so.seg : 0;
+  const int t_end = SPLIT ? min(ntiles, t_beg + so.seg) : ntiles;
+  if (SPLIT && t_beg >= t_end) return;  // the query tile's keys end before this segment
 
   const size_t head = (size_t)bh * N * D;
   const uint32_t head_bytes = (uint32_t)N * D * 2u;
@@ -359,14 +412,12 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void bwd_dq_kernel(
       for (int s = 0; s < KSTEPS; ++s) c[s] = nc[s];
     }
     dlt = halves_sum(c[0]) * delta_mult;
-    if (g == 0 && qi < N) Delta[(size_t)bh * N + qi] = -dlt;
+    if (g == 0 && qi < N && sg == 0) Delta[(size_t)bh * N + qi] = -dlt;
   } else {
     const auto rdel = make_rsrc(Delta + (size_t)bh * N, (uint32_t)N * 4u);
     dlt = -__uint_as_float(buf_load4(rdel, (uint32_t)qi * 4u));
   }
 
-  const int kv_end = CAUSAL ? min(N, q0 + kBR) : N;
-  const int ntiles = (kv_end + kBC - 1) / kBC;
   const FragOffsets<L> fo(lane);
 
   f32x16 qacc[DB];  // dQᵀ: rows d = 32b + 8(r/4) + 4g + r%4, column = this lane's query
@@ -375,15 +426,16 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void bwd_dq_kernel(
 #pragma unroll
     for (int r = 0; r < 16; ++r) qacc[b][r] = 0.f;
 
-  copy(mk, 0, k0s);
-  copy(mv, 0, v0s);
+  copy(mk, t_beg * kBC, k0s);
+  copy(mv, t_beg * kBC, v0s);
   wait_vmem_all();
   __syncthreads();
 
-  // One key tile; P is its parity (compile-time), the tile is in buffers P, buffers P^1 are free.
+  // One key tile; P is the parity of j − t_beg (compile-time), the tile is in buffers P, buffers P^1
+  // are free.
   auto tile_fn = [&](auto parity, int j) {
     constexpr int P = decltype(parity)::value;
-    if (j + 1 < ntiles) {
+    if (j + 1 < t_end) {
       copy(mk, (j + 1) * kBC, P ? k0s : k1s);
       copy(mv, (j + 1) * kBC, P ? v0s : v1s);
     }
@@ -442,9 +494,23 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void bwd_dq_kernel(
     __syncthreads();
   };
 
-  for (int j = 0; j < ntiles; j += 2) {
+  for (int j = t_beg; j < t_end; j += 2) {
     tile_fn(std::integral_constant<int, 0>{}, j);
-    if (j + 1 < ntiles) tile_fn(std::integral_constant<int, 1>{}, j + 1);
+    if (j + 1 < t_end) tile_fn(std::integral_constant<int, 1>{}, j + 1);
+  }
+
+  if constexpr (SPLIT) {
+    // The segment's unscaled dQᵀ sums for this lane's query (d rows 32b + 8(r/4) + 4g + 0..3).
+    if (qi < N) {
+      float* qr = so.part_a + (((size_t)sg * so.bh_count + bh) * N + qi) * D;
+#pragma unroll
+      for (int b = 0; b < DB; ++b)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4)
+          *(f32x4*)&qr[32 * b + 8 * r4 + 4 * g] = f32x4{qacc[b][4 * r4], qacc[b][4 * r4 + 1],
+                                                        qacc[b][4 * r4 + 2], qacc[b][4 * r4 + 3]};
+    }
+    return;
   }
 
   if (qi < N) {
@@ -477,10 +543,10 @@ hipError_t launch_dkdv_pass(const BwdArgs& a, hipStream_t stream) {
   const int nkt = (a.N + kBKV - 1) / kBKV;
   const uint32_t total = (uint32_t)a.B * a.H * nkt;
   const int remap = use_xcd_order(total, (long)a.B * a.H, CAUSAL ? 1 : 0);
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, OUT>), dim3(total), dim3(kThreads), 0, stream,
-                     (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, a.lse,
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, OUT, false>), dim3(total), dim3(kThreads), 0,
+                     stream, (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, a.lse,
                      (const bf16*)a.dout, (const float*)a.delta, (bf16*)a.dk, (bf16*)a.dv, a.N, nkt,
-                     a.dk_scale, a.scale * kLog2e, remap);
+                     a.dk_scale, a.scale * kLog2e, remap, BwdSplitOut{});
   return hipGetLastError();
 }
 
@@ -500,10 +566,85 @@ hipError_t launch_dq(const BwdArgs& a, hipStream_t stream) {
   const int nqt = (a.N + kBR - 1) / kBR;
   const uint32_t total = (uint32_t)a.B * a.H * nqt;
   const int remap = use_xcd_order(total, (long)a.B * a.H, CAUSAL ? 1 : 0);
-  hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, WITH_D>), dim3(total), dim3(kThreads), 0, stream,
+  hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, WITH_D, false>), dim3(total), dim3(kThreads), 0,
+                     stream, (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, a.lse,
+                     (const bf16*)a.dout, a.delta, (const bf16*)a.o, (bf16*)a.dq, a.N, nqt,
+                     a.dq_scale, a.scale * kLog2e, a.delta_mult, remap, BwdSplitOut{});
+  return hipGetLastError();
+}
+
+// Split backward, last step: per row, the sum of its segments' partial dQ (segments of the row's query
+// tile's key range) and partial dK, dV (segments of the row's key block's query range), scaled and
+// rounded to bf16.  One thread per four consecutive values of a row.
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kThreads) void bwd_split_reduce_kernel(
+    const float* __restrict__ part_dq, const float* __restrict__ part_dk,
+    const float* __restrict__ part_dv, bf16* __restrict__ dQ, bf16* __restrict__ dK,
+    bf16* __restrict__ dV, int N, int bh_count, int seg, float dq_scale, float dk_scale) {
+  constexpr int C = D / 4;
+  const size_t rows = (size_t)bh_count * N;
+  const size_t idx = (size_t)blockIdx.x * kThreads + threadIdx.x;
+  if (idx >= rows * C) return;
+  const size_t row = idx / C;
+  const size_t off = row * D + 4 * (idx % C);
+  const size_t stride = rows * D;  // from one segment's array to the next
+  const int i = (int)(row % (size_t)N);
+  const int kv_end = CAUSAL ? min(N, (i / kBR + 1) * kBR) : N;
+  const int nq = ((kv_end + kBC - 1) / kBC + seg - 1) / seg;
+  const int qstart = CAUSAL ? (i / kBKV) * kBKV : 0;
+  const int nk = ((N - qstart + kBQ - 1) / kBQ + 2 * seg - 1) / (2 * seg);
+  f32x4 q = {0.f, 0.f, 0.f, 0.f}, k = q, v = q;
+  for (int sg = 0; sg < nq; ++sg) q += *(const f32x4*)(part_dq + sg * stride + off);
+  for (int sg = 0; sg < nk; ++sg) {
+    k += *(const f32x4*)(part_dk + sg * stride + off);
+    v += *(const f32x4*)(part_dv + sg * stride + off);
+  }
+  auto store4 = [](bf16* p, f32x4 x, float m) {
+    u32x2 w;
+    w[0] = pack_bf16x2(x[0] * m, x[1] * m);
+    w[1] = pack_bf16x2(x[2] * m, x[3] * m);
+    *(u32x2*)p = w;
+  };
+  store4(dQ + off, q, dq_scale);
+  store4(dK + off, k, dk_scale);
+  store4(dV + off, v, 1.f);
+}
+
+// The whole split backward: D and the dQ partial sums (one dQ launch, or bwd_pre first at d = 96),
+// the dK/dV partial sums, then the reduction.  Work items are segment-major and dealt round-robin to
+// the XCDs, as in the split forward.
+template <int D, bool CAUSAL>
+hipError_t launch_bwd_split(const BwdArgs& a, hipStream_t stream) {
+  const BwdSplit sp = bwd_split(a.B, a.H, a.N, D, CAUSAL ? 1 : 0);
+  const int bh = a.B * a.H;
+  const int nqt = (a.N + kBR - 1) / kBR;
+  const BwdSplitOut sq{a.part_dq, nullptr, sp.seg, bh};
+  if constexpr (D == 96) {
+    hipError_t e = launch_pre<96>(a, stream);
+    if (e != hipSuccess) return e;
+  }
+  constexpr bool kWithD = D != 96;
+  hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, kWithD, true>),
+                     dim3((uint32_t)sp.nseg_q * bh * nqt), dim3(kThreads), 0, stream,
                      (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, a.lse,
                      (const bf16*)a.dout, a.delta, (const bf16*)a.o, (bf16*)a.dq, a.N, nqt,
-                     a.dq_scale, a.scale * kLog2e, a.delta_mult, remap);
+                     a.dq_scale, a.scale * kLog2e, a.delta_mult, 0, sq);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int nkt = (a.N + kBKV - 1) / kBKV;
+  const BwdSplitOut sk{a.part_dk, a.part_dv, 2 * sp.seg, bh};
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, 3, true>), dim3((uint32_t)sp.nseg_k * bh * nkt),
+                     dim3(kThreads), 0, stream, (const bf16*)a.q, (const bf16*)a.k,
+                     (const bf16*)a.v, a.lse, (const bf16*)a.dout, (const float*)a.delta,
+                     (bf16*)a.dk, (bf16*)a.dv, a.N, nkt, a.dk_scale, a.scale * kLog2e, 0, sk);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const size_t chunks = (size_t)bh * a.N * (D / 4);
+  hipLaunchKernelGGL((bwd_split_reduce_kernel<D, CAUSAL>),
+                     dim3((uint32_t)((chunks + kThreads - 1) / kThreads)), dim3(kThreads), 0, stream,
+                     (const float*)a.part_dq, (const float*)a.part_dk, (const float*)a.part_dv,
+                     (bf16*)a.dq, (bf16*)a.dk, (bf16*)a.dv, a.N, bh, sp.seg, a.dq_scale,
+                     a.dk_scale);
   return hipGetLastError();
 }
 
@@ -550,6 +691,16 @@ hipError_t launch_bwd_delta_dq(const BwdArgs& a, hipStream_t stream) {
 }
 
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream) {
+  if (a.split_seg > 0) {  // bwd_split chose a split (head dimensions up to 128)
+    if (a.d == 64)
+      return a.causal ? launch_bwd_split<64, true>(a, stream) : launch_bwd_split<64, false>(a, stream);
+    if (a.d == 96)
+      return a.causal ? launch_bwd_split<96, true>(a, stream) : launch_bwd_split<96, false>(a, stream);
+    if (a.d == 128)
+      return a.causal ? launch_bwd_split<128, true>(a, stream)
+                      : launch_bwd_split<128, false>(a, stream);
+    return hipErrorInvalidValue;
+  }
   const hipError_t e = launch_bwd_delta_dq(a, stream);
   return e == hipSuccess ? launch_bwd_dkdv(a, stream) : e;
 }

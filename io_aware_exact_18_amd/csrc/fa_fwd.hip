@@ -125,6 +125,13 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
   const int qw = q0 + wave * 32;  // first query of this wave
   const int qi = qw + lc;         // this lane's query
 
+  const int kv_end = CAUSAL ? min(N, q0 + kBR) : N;
+  const int ntiles = (kv_end + kBC - 1) / kBC;
+  // Key tiles [t_beg, t_end) of this workgroup: all of them, or one segment of the split.
+  const int t_beg = SPLIT ? sg * so.seg : 0;
+  const int t_end = SPLIT ? min(ntiles, t_beg + so.seg) : ntiles;
+  if (SPLIT && t_beg >= t_end) return;  // the query tile's keys end before this segment
+
   const size_t head = (size_t)bh * N * D;
   const uint32_t head_bytes = (uint32_t)N * D * 2u;
   const auto rq = make_rsrc(Q + head, head_bytes);
@@ -138,12 +145,6 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
   for (int s = 0; s < KSTEPS; ++s)
     qf[s] = __builtin_bit_cast(bf16x8, buf_load16(rq, (uint32_t)(qi * D + 16 * s + 8 * g) * 2u));
 
-  const int kv_end = CAUSAL ? min(N, q0 + kBR) : N;
-  const int ntiles = (kv_end + kBC - 1) / kBC;
-  // Key tiles [t_beg, t_end) of this workgroup: all of them, or one segment of the split.
-  const int t_beg = SPLIT ? sg * so.seg : 0;
-  const int t_end = SPLIT ? min(ntiles, t_beg + so.seg) : ntiles;
-  if (SPLIT && t_beg >= t_end) return;  // the query tile's keys end before this segment
   // Tiles at or beyond this index are fully masked for this wave (causal): no math on them.
   const int wave_tiles = CAUSAL ? min(t_end, (qw + 31) / kBC + 1) : t_end;
   const FragOffsets<L> fo(lane);

@@ -44,6 +44,11 @@ struct BwdArgs {
   float dk_scale = 0.f;    // dK = dk_scale · Σ_i dS_ij q_i and dQ = dq_scale · Σ_j dS_ij k_j, with
   float dq_scale = 0.f;    // dS computed from v as stored and D; both equal `scale` for bf16 inputs
   float delta_mult = 1.f;  // 1 for bf16 inputs; 1 / v_descale when v holds e4m3 codes
+  // Split backward (bwd_split): seg > 0 selects it; the partial sums live in the workspace after D.
+  int split_seg = 0;
+  float* part_dq = nullptr;
+  float* part_dk = nullptr;
+  float* part_dv = nullptr;
 };
 
 struct DecodeArgs {
@@ -146,6 +151,26 @@ inline size_t fwd_split_workspace_bytes(int B, int H, int N, int d, int causal) 
   return (((size_t)sp.nseg * B * H * N * ((size_t)d + 3) * sizeof(float)) + 255u) & ~(size_t)255u;
 }
 
+// Split backward, for the same grids: the dQ kernel (128-query tiles over 64-key tiles, the forward's
+// geometry) splits each tile's key range into fwd_split's segments of `seg` tiles; the dK/dV kernel
+// (128-key blocks over 32-query steps) splits each block's query range into segments of 2·seg steps,
+// i.e. the same number of rows.  Each segment writes fp32 partial sums; one more kernel adds a row's
+// segments, scales and rounds to bf16.
+struct BwdSplit {
+  int seg;     // 0: no split; else fwd_split's segment length in 64-key tiles
+  int nseg_q;  // segments of the longest key range (dQ kernel)
+  int nseg_k;  // segments of the longest query range (dK/dV kernel)
+};
+inline BwdSplit bwd_split(int B, int H, int N, int d, int causal) {
+  const FwdSplit f = fwd_split(B, H, N, d, causal);
+  if (f.nseg <= 1) return BwdSplit{0, 1, 1};
+  const long steps = ((long)N + 31) / 32;
+  return BwdSplit{f.seg, f.nseg, (int)((steps + 2L * f.seg - 1) / (2L * f.seg))};
+}
+inline size_t bwd_split_part_bytes(int nseg, int B, int H, int N, int d) {
+  return (((size_t)nseg * B * H * N * (size_t)d * sizeof(float)) + 255u) & ~(size_t)255u;
+}
+
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_fwd_fp8(const Fp8FwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd_pre(const BwdArgs& a, hipStream_t stream);
@@ -172,6 +197,16 @@ inline size_t bwd_fp8_image_bytes(int B, int H, int N, int d) {
 }
 inline size_t bwd_fp8_workspace_bytes(int B, int H, int N, int d) {
   return bwd_delta_bytes(B, H, N) + 3 * bwd_fp8_image_bytes(B, H, N, d);
+}
+// Split backward workspace: D, then the dQ partial sums, then the dK and dV partial sums; just D
+// when the shape is not split.
+inline size_t bwd_split_workspace_bytes(int B, int H, int N, int d, int causal) {
+  const BwdSplit sp = bwd_split(B, H, N, d, causal);
+  size_t bytes = bwd_delta_bytes(B, H, N);
+  if (sp.seg > 0)
+    bytes += bwd_split_part_bytes(sp.nseg_q, B, H, N, d) +
+             2 * bwd_split_part_bytes(sp.nseg_k, B, H, N, d);
+  return bytes;
 }
 
 }  // namespace fa

@@ -26,6 +26,9 @@ def lib():
     lib.fa_fwd_split_workspace_bytes.argtypes = [i, i, i, i, i]
     lib.fa_fwd_split_workspace_bytes.restype = sz
     lib.fa_fwd_split.argtypes = [vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, f, vp]
+    lib.fa_bwd_split_workspace_bytes.argtypes = [i, i, i, i, i]
+    lib.fa_bwd_split_workspace_bytes.restype = sz
+    lib.fa_bwd_split.argtypes = [vp] * 10 + [sz, i, i, i, i, i, f, vp]
     lib.fa_fwd_fp8.argtypes = [vp, vp, vp, f, f, f, vp, vp, i, i, i, i, i, f, vp]
     lib.fa_bwd_workspace_bytes.argtypes = [i, i, i, i]
     lib.fa_bwd_workspace_bytes.restype = sz
@@ -48,7 +51,8 @@ def lib():
 def test_exports_match_header(lib):
     text = open(HEADER).read()
     declared = set(re.findall(r"^\s*(?:fa_status|size_t|const char\*)\s+(fa_\w+)\s*\(", text, re.M))
-    assert declared == {"fa_fwd", "fa_fwd_split", "fa_fwd_split_workspace_bytes", "fa_fwd_fp8", "fa_bwd_workspace_bytes", "fa_bwd", "fa_status_str",
+    assert declared == {"fa_fwd", "fa_fwd_split", "fa_fwd_split_workspace_bytes", "fa_bwd_split",
+                        "fa_bwd_split_workspace_bytes", "fa_fwd_fp8", "fa_bwd_workspace_bytes", "fa_bwd", "fa_status_str",
                         "fa_bwd_preprocess", "fa_bwd_dkdv", "fa_bwd_dq", "fa_device_info",
                         "fa_decode", "fa_decode_workspace_bytes", "fa_bwd_fp8",
                         "fa_bwd_fp8_workspace_bytes", "fa_bwd_noalloc", "fa_bwd_noalloc_max_rows",
@@ -149,6 +153,45 @@ def test_fwd_split_rejections(lib):
     assert fwd_split(lib, ws=None) == WORKSPACE
     assert fwd_split(lib, ws_bytes=need - 1) == WORKSPACE
     assert fwd_split(lib, ws=P + 16) == ALIGN
+
+
+def test_bwd_split_workspace_formula(lib):
+    """fa.h: D bytes, then (when split) nseg_q + 2·nseg_k partial arrays of B·H·N·d fp32, each rounded
+    up to 256 bytes; fa_bwd's size when not split."""
+    r256 = lambda x: -(-x // 256) * 256
+    seen = 0
+    for B, H, N, d, causal in ((1, 1, 16384, 128, 1), (1, 1, 65536, 128, 1), (1, 3, 5000, 96, 0),
+                               (1, 1, 1025, 64, 1), (4, 32, 4096, 128, 1), (1, 1, 65536, 256, 1),
+                               (2, 4, 8192, 128, 1), (1, 2, 8192, 64, 1)):
+        seg, nseg = _fwd_split(B, H, N, d, causal)
+        want = r256(B * H * N * 4)
+        if nseg > 1:
+            seen += 1
+            nseg_k = -(-(-(-N // 32)) // (2 * seg))
+            want += r256(nseg * B * H * N * d * 4) + 2 * r256(nseg_k * B * H * N * d * 4)
+        else:
+            assert want == lib.fa_bwd_workspace_bytes(B, H, N, d)
+        assert lib.fa_bwd_split_workspace_bytes(B, H, N, d, causal) == want, (B, H, N, d, causal)
+    assert seen >= 4
+    for bad in ((0, 1, 8, 64, 1), (1, 1, 8, 80, 1), (1, 1, 1 << 23, 128, 1)):
+        assert lib.fa_bwd_split_workspace_bytes(*bad) == 0, bad
+
+
+def bwd_split(lib, ws=P, ws_bytes=1 << 34, q=P, dq=P, N=16384, d=128, causal=1, scale=0.125):
+    return lib.fa_bwd_split(q, P, P, P, P, P, dq, P, P, ws, ws_bytes, 1, 1, N, d, causal, scale, None)
+
+
+def test_bwd_split_rejections(lib):
+    assert bwd_split(lib, q=None) == NULL
+    assert bwd_split(lib, N=0) == SHAPE
+    assert bwd_split(lib, d=80) == UNSUP
+    assert bwd_split(lib, scale=0.0) == UNSUP
+    assert bwd_split(lib, dq=MIS) == ALIGN
+    assert bwd_split(lib, ws=None) == WORKSPACE
+    need = lib.fa_bwd_split_workspace_bytes(1, 1, 16384, 128, 1)
+    assert need > lib.fa_bwd_workspace_bytes(1, 1, 16384, 128)  # the split's partial sums
+    assert bwd_split(lib, ws_bytes=need - 1) == WORKSPACE
+    assert bwd_split(lib, ws=P + 16) == ALIGN
 
 
 def test_fwd_fp8_rejections(lib):

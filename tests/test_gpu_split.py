@@ -142,3 +142,133 @@ def test_fwd_split_workspace_reuse_with_smaller_shape():
     o2, l2 = fa().fwd_split(q2, k2, v2, True, workspace=ws)
     torch.cuda.synchronize()
     _check_rows(q2.cpu(), k2.cpu(), v2.cpu(), o2, l2, True, 1.0 / math.sqrt(128))
+
+
+# ------------------------------------------------------------------------------------------------
+# Split backward (fa_bwd_split).  Each gradient is a sum over keys (dQ) or queries (dK, dV); the
+# split only groups those sums differently, so the oracle bound is the backward's (relative Frobenius
+# error ≤ 2e-2) and split and unsplit gradients agree to fp32 summation order plus one bf16 rounding.
+
+GRAD_TOL, SAME_TOL = 2e-2, 4e-3
+
+
+def _rel_fro(got, ref):
+    den = np.linalg.norm(ref)
+    return np.linalg.norm(got - ref) / (den if den > 0 else 1.0)
+
+
+def _bwd_both(q, k, v, do, causal, scale, workspace=None):
+    """Forward, then the split and the unsplit backward of the same inputs (device tensors)."""
+    o, lse = fa().fwd(q, k, v, causal, scale)
+    split = fa().bwd_split(q, k, v, o, lse, do, causal, scale, workspace=workspace)
+    plain = fa().bwd(q, k, v, o, lse, do, causal, scale)
+    torch.cuda.synchronize()
+    return split, plain
+
+
+def _check_bwd_oracle(q, k, v, do, grads, causal, scale):
+    B, H, N, d = q.shape
+    worst = 0.0
+    for h in range(B * H):
+        b, hh = divmod(h, H)
+        ref = oracle.attention_head_bwd64(*(_np64(x[b, hh]) for x in (q, k, v, do)), causal, scale)
+        for got, r, name in zip(grads, ref, ("dq", "dk", "dv")):
+            g = _np64(got[b, hh])
+            assert np.all(np.isfinite(g)), (h, name)
+            e = _rel_fro(g, r)
+            assert e <= GRAD_TOL, (h, name, e)
+            worst = max(worst, e)
+    return worst
+
+
+def _check_same(split, plain):
+    worst = 0.0
+    for s, p, name in zip(split, plain, ("dq", "dk", "dv")):
+        e = _rel_fro(_np64(s), _np64(p))
+        assert e <= SAME_TOL, (name, e)
+        worst = max(worst, e)
+    return worst
+
+
+SPLIT_BWD = [(1, 1, n, d, c) for d in (64, 96, 128) for c in (False, True) for n in (1025, 2000, 3001)]
+
+
+@pytest.mark.parametrize("B,H,N,d,causal", SPLIT_BWD)
+def test_bwd_split_small(B, H, N, d, causal):
+    """One head long enough to be split, ragged lengths included: dQ, dK, dV against the oracle and
+    against the unsplit backward."""
+    assert fa().bwd_split_workspace_bytes(B, H, N, d, causal) > fa().bwd_workspace_bytes(B, H, N, d)
+    q, k, v = _inputs(B, H, N, d, seed=7 * N + d + int(causal))
+    do = _inputs(B, H, N, d, seed=7 * N + d + 99)[0]
+    scale = 1.0 / math.sqrt(d)
+    split, plain = _bwd_both(q.cuda(), k.cuda(), v.cuda(), do.cuda(), causal, scale)
+    e_o = _check_bwd_oracle(q, k, v, do, split, causal, scale)
+    e_s = _check_same(split, plain)
+    print(f"PARITY bwd_split {B}x{H}x{N}x{d} causal={causal}: oracle {e_o:.3g} vs unsplit {e_s:.3g}")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_split_several_heads(causal):
+    B, H, N, d = 1, 3, 5000, 128
+    assert fa().bwd_split_workspace_bytes(B, H, N, d, causal) > fa().bwd_workspace_bytes(B, H, N, d)
+    q, k, v = _inputs(B, H, N, d, seed=5100 + int(causal))
+    do = _inputs(B, H, N, d, seed=5200)[0]
+    scale = 1.0 / math.sqrt(d)
+    split, plain = _bwd_both(q.cuda(), k.cuda(), v.cuda(), do.cuda(), causal, scale)
+    e_o = _check_bwd_oracle(q, k, v, do, split, causal, scale)
+    e_s = _check_same(split, plain)
+    print(f"PARITY bwd_split {B}x{H}x{N}x{d} causal={causal}: oracle {e_o:.3g} vs unsplit {e_s:.3g}")
+
+
+def test_bwd_split_long_head():
+    """One causal head of 16384 keys: split against unsplit gradients, dQ row blocks at the start, the
+    middle and the end against the oracle's row-restricted form, the exact sums Σ dV = Σ dO and
+    Σ dK = 0, and bit-identical repeated calls."""
+    B, H, N, d, causal = 1, 1, 16384, 128, True
+    q, k, v = _inputs(B, H, N, d, seed=16384, device="cuda")
+    do = _inputs(B, H, N, d, seed=16385, device="cuda")[0]
+    scale = 1.0 / math.sqrt(d)
+    split, plain = _bwd_both(q, k, v, do, causal, scale)
+    o, lse = fa().fwd(q, k, v, causal, scale)
+    again = fa().bwd_split(q, k, v, o, lse, do, causal, scale)
+    torch.cuda.synchronize()
+    assert all(torch.equal(a, b) for a, b in zip(split, again))
+    e_s = _check_same(split, plain)
+    q64, k64, v64, do64 = (_np64(x[0, 0]) for x in (q, k, v, do))
+    dq_c = split[0][0, 0].cpu()
+    for r0 in (0, N // 2 - 4, N - 8):
+        rows = list(range(r0, r0 + 8))
+        ref = oracle.attention_rows_dq64(q64, k64, v64, do64, rows, causal, scale)
+        assert _rel_fro(_np64(dq_c[r0:r0 + 8]), ref) <= GRAD_TOL, r0
+    dq, dk, dv = split
+    sdv, sdo = dv.double().sum(dim=2), do.double().sum(dim=2)
+    assert ((sdv - sdo).norm(dim=-1) / sdo.norm(dim=-1)).max().item() <= GRAD_TOL
+    assert (dk.double().sum(dim=2).norm(dim=-1) / dk.double().norm(dim=(2, 3))).max().item() <= GRAD_TOL
+    print(f"PARITY bwd_split 1x1x{N}x{d} causal: vs unsplit {e_s:.3g}")
+
+
+def test_bwd_split_unsplit_shapes_equal_bwd():
+    """Shapes that are not split need fa_bwd's workspace only, and fa_bwd_split then gives fa_bwd's
+    gradients bit for bit."""
+    for B, H, N, d, causal in ((16, 16, 1024, 64, True), (1, 1, 1024, 96, False),
+                               (1, 1, 3000, 256, True)):
+        assert fa().bwd_split_workspace_bytes(B, H, N, d, causal) == fa().bwd_workspace_bytes(B, H, N, d)
+        q, k, v = _inputs(B, H, N, d, seed=B * H + N + 1, device="cuda")
+        do = _inputs(B, H, N, d, seed=B * H + N + 2, device="cuda")[0]
+        split, plain = _bwd_both(q, k, v, do, causal, 1.0 / math.sqrt(d))
+        assert all(torch.equal(a, b) for a, b in zip(split, plain)), (B, H, N, d)
+
+
+def test_bwd_split_workspace_reuse_with_smaller_shape():
+    """One workspace, two calls in a row, the second on a smaller split shape."""
+    need = fa().bwd_split_workspace_bytes(1, 1, 6000, 128, True)
+    assert need >= fa().bwd_split_workspace_bytes(1, 1, 2100, 64, True) > 0
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    q, k, v = _inputs(1, 1, 6000, 128, seed=71, device="cuda")
+    do = _inputs(1, 1, 6000, 128, seed=72, device="cuda")[0]
+    _bwd_both(q, k, v, do, True, 1.0 / math.sqrt(128), workspace=ws)
+    q, k, v = _inputs(1, 1, 2100, 64, seed=73)
+    do = _inputs(1, 1, 2100, 64, seed=74)[0]
+    split, plain = _bwd_both(q.cuda(), k.cuda(), v.cuda(), do.cuda(), True, 0.125, workspace=ws)
+    _check_bwd_oracle(q, k, v, do, split, True, 0.125)
+    _check_same(split, plain)
