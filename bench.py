@@ -426,6 +426,70 @@ def fwd_bwd_secondary(fa, workloads, lib, name, steps, warmup):
     return out
 
 
+def split_secondary(fa, workloads, lib, name, steps, warmup):
+    """Secondary measurement: forward + backward of a workload with too few query tiles to fill the
+    device, once through fa_fwd + fa_bwd and once through the key-range split entry points
+    (fa_fwd_split + fa_bwd_split) on the same inputs; each step bracketed by events."""
+    import torch
+    w = workloads.WORKLOADS[name]
+    B, H, N, d = w.shape()
+    log(f"[bench] secondary: {name} forward+backward, unsplit and split, B={B} H={H} N={N} d={d}")
+    inp = workloads.make_inputs(name)
+    dev = torch.device("cuda:0")
+    q, k, v, do = (inp[x].to(dev) for x in ("q", "k", "v", "do"))
+    del inp
+    o, dq, dk, dv = (torch.empty_like(q) for _ in range(4))
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    c = int(w.causal)
+    ws_f = fa.fwd_split_workspace_bytes(B, H, N, d, c)
+    ws_b = fa.bwd_split_workspace_bytes(B, H, N, d, c)
+    ws = torch.empty(max(ws_f, ws_b, 256), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    sp = stream.cuda_stream
+    ptrs = [x.data_ptr() for x in (q, k, v, o, lse, do, dq, dk, dv)]
+
+    def check(fn, code):
+        if code != 0:
+            raise fa.FaError(fn, code, fa.status_str(code))
+
+    def plain(ev):
+        ev[0].record(stream)
+        check("fa_fwd", lib.fa_fwd(*ptrs[:5], B, H, N, d, c, w.scale, sp))
+        ev[1].record(stream)
+        check("fa_bwd", lib.fa_bwd(*ptrs, ws.data_ptr(), ws.numel(), B, H, N, d, c, w.scale, sp))
+        ev[2].record(stream)
+
+    def split(ev):
+        ev[0].record(stream)
+        check("fa_fwd_split", lib.fa_fwd_split(*ptrs[:5], ws.data_ptr(), ws.numel(), B, H, N, d, c,
+                                               w.scale, sp))
+        ev[1].record(stream)
+        check("fa_bwd_split", lib.fa_bwd_split(*ptrs, ws.data_ptr(), ws.numel(), B, H, N, d, c,
+                                               w.scale, sp))
+        ev[2].record(stream)
+
+    fwd_f, bwd_f = w.fwd_flops(), w.bwd_flops()
+    out = {"workload": name, "peak": BF16_PEAK_TFLOPS, "bound": "mfma", "flops": fwd_f + bwd_f,
+           "fwd_split_workspace_bytes": ws_f, "bwd_split_workspace_bytes": ws_b}
+    for label, fn in (("unsplit", plain), ("split", split)):
+        spare = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        for _ in range(warmup):
+            fn(spare)
+        events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+        for i in range(steps):
+            fn(events[i])
+        torch.cuda.synchronize(dev)
+        f_ms = sum(e[0].elapsed_time(e[1]) for e in events) / steps
+        b_ms = sum(e[1].elapsed_time(e[2]) for e in events) / steps
+        out[label] = {"ms": f_ms + b_ms, "fwd_ms": f_ms, "bwd_ms": b_ms,
+                      "tflops": (fwd_f + bwd_f) / ((f_ms + b_ms) * 1e-3) / 1e12,
+                      "fwd_tflops": fwd_f / (f_ms * 1e-3) / 1e12,
+                      "bwd_tflops": bwd_f / (b_ms * 1e-3) / 1e12}
+    del q, k, v, do, o, dq, dk, dv, lse, ws
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -444,8 +508,9 @@ def main():
                     help="skip the secondary measurements at head dimensions 256 and 96 "
                          "(d256_4k, d96_4k workloads)")
     ap.add_argument("--no-configs", action="store_true",
-                    help="skip the secondary measurements of the d64_2k and long_16k workloads "
-                         "(long_16k runs the causal d=128 kernel instantiations)")
+                    help="skip the secondary measurements of the d64_2k, long_16k and "
+                         "onehead_32k workloads (long_16k runs the causal d=128 kernel "
+                         "instantiations, onehead_32k their split forms)")
     ap.add_argument("--no-decode", action="store_true",
                     help="skip the secondary decoding measurements (decode_32k, specdec_32k)")
     ap.add_argument("--traffic-sweep", action="store_true",
@@ -601,6 +666,8 @@ def main():
         for name in ("d64_2k", "long_16k"):
             secondary[name + "_fwd_bwd"] = fwd_bwd_secondary(fa, workloads, lib, name, args.steps,
                                                              args.warmup)
+        secondary["onehead_32k_fwd_bwd"] = split_secondary(fa, workloads, lib, "onehead_32k",
+                                                           args.steps, args.warmup)
     if not args.no_decode:
         secondary.update(decode_measure(fa, workloads, lib, args.steps, args.warmup))
 

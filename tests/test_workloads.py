@@ -8,7 +8,8 @@ import workloads
 
 def test_workload_table():
     w = workloads.WORKLOADS
-    assert [x.number for x in w.values()] == [1, 2, 3, 4, 5, 8, 9, 10, 11, 12, 13]
+    assert [x.number for x in w.values()] == [1, 2, 3, 4, 5, 8, 9, 10, 11, 12, 13, 14]
+    assert w["onehead_32k"].shape() == (1, 1, 32768, 128) and w["onehead_32k"].backward
     assert w["fp8bwd_8k"].fp8 and w["fp8bwd_8k"].backward
     assert w["d96_4k"].shape() == (4, 32, 4096, 96)
     assert w["d256_4k"].shape() == (4, 16, 4096, 256) and w["d256_4k"].causal

@@ -22,6 +22,8 @@ fp8bwd_8k 4, 32, 8192, 128       yes     fp8 forward + backward: e4m3 Q/K/V as f
 fp8_d64_8k 4, 32, 8192, 64       yes     fp8 forward only, as fp8_8k at head dimension 64
 fp8_d96_8k 4, 32, 8192, 96       yes     fp8 forward only, as fp8_8k at head dimension 96
 fp8_d256_8k 4, 16, 8192, 256     yes     fp8 forward only, head dimension 256 (the FLOPs of fp8_8k)
+onehead_32k 1, 1, 32768, 128     yes     forward + backward, bf16, one head: too few query tiles to
+                                         fill the device unsplit (the split forward and backward)
 ========  =====================  ======  ========================================================
 
 Decoding workloads (queries [B, H, Nq, d] against a key/value cache [B, H, Nk, d]; the queries are the
@@ -35,7 +37,7 @@ specdec_32k  4, 32, 8, 32768, 128        yes     8 draft tokens verified at once
 ===========  ==========================  ======  ===================================================
 
 Seeds: tensor t of workload c uses ``torch.Generator().manual_seed(1000*c + t)`` with c the workload
-number 1..13 and t = 0 (Q), 1 (K), 2 (V), 3 (dO), 4 (positions of the enlarged keys).  Values are drawn
+number 1..14 and t = 0 (Q), 1 (K), 2 (V), 3 (dO), 4 (positions of the enlarged keys).  Values are drawn
 as float32 N(0, 1) on the CPU and rounded to the storage type, so every consumer sees identical inputs.
 """
 
@@ -93,6 +95,7 @@ WORKLOADS = {
         Workload(11, "fp8_d64_8k", 4, 32, 8192, 64, causal=True, backward=False, fp8=True),
         Workload(12, "fp8_d96_8k", 4, 32, 8192, 96, causal=True, backward=False, fp8=True),
         Workload(13, "fp8_d256_8k", 4, 16, 8192, 256, causal=True, backward=False, fp8=True),
+        Workload(14, "onehead_32k", 1, 1, 32768, 128, causal=True, backward=True),
     ]
 }
 
