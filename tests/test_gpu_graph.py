@@ -1,5 +1,6 @@
-"""The library under HIP graph capture.  Every entry point (forward, backward, decoding, and the FP8
-forward and backward) is captured into one graph through the current stream and replayed.  The
+"""The library under HIP graph capture.  Every entry point (forward, backward, decoding, the FP8
+forward and backward, and the split forward and backward on a shape they split) is captured into one
+graph through the current stream and replayed.  The
 kernels are deterministic, so each replay must reproduce the eager results bit for bit, also with
 eager work between replays and after the captured input tensors are refilled in place.  One head of
 the replayed results is also checked against the fp64 oracle.
@@ -30,6 +31,7 @@ def fa():
 
 
 B, H, N, D, NQ = 1, 3, 333, 128, 6
+NL = 1100  # one head of NL keys: 18 key tiles, split by fa_fwd_split / fa_bwd_split
 SCALE = 1.0 / math.sqrt(D)
 S8 = (0.011, 0.013, 0.009)  # descales of the e4m3 inputs (any positive values are valid)
 
@@ -37,7 +39,7 @@ S8 = (0.011, 0.013, 0.009)  # descales of the e4m3 inputs (any positive values a
 def _fill(bufs, seed):
     """Refill the captured input tensors in place with new seeded values."""
     g = torch.Generator().manual_seed(seed)
-    for t in bufs["bf16"]:
+    for t in bufs["bf16"] + bufs["long"]:
         t.copy_(torch.randn(t.shape, generator=g).to(torch.bfloat16))
     for t in bufs["e4m3"]:  # e4m3 codes spread over most of the format's range
         t.copy_((torch.randn(t.shape, generator=g) * 100.0).clamp(-448.0, 448.0)
@@ -54,7 +56,10 @@ def _work(bufs, ws):
     od, ld = fa().decode(bufs["qdec"], k, v, True, SCALE, workspace=ws["dec"])
     o8, l8 = fa().fwd_fp8(q8, k8, v8, *S8, True, SCALE)
     g8 = fa().bwd_fp8(q8, k8, v8, *S8, o8, l8, do, True, SCALE, workspace=ws["bwd8"])
-    return [o, lse, dq, dk, dv, od, ld, o8, l8, *g8]
+    ql, kl, vl, dol = bufs["long"]
+    os_, ls_ = fa().fwd_split(ql, kl, vl, True, SCALE, workspace=ws["fsplit"])
+    gs = fa().bwd_split(ql, kl, vl, os_, ls_, dol, True, SCALE, workspace=ws["bsplit"])
+    return [o, lse, dq, dk, dv, od, ld, o8, l8, *g8, os_, ls_, *gs]
 
 
 def test_graph_capture_and_replay_match_eager():
@@ -62,12 +67,18 @@ def test_graph_capture_and_replay_match_eager():
     bufs = {"bf16": [torch.empty(B, H, N, D, dtype=torch.bfloat16, device=dev) for _ in range(4)],
             "e4m3": [torch.empty(B, H, N, D, dtype=torch.float8_e4m3fn, device=dev)
                      for _ in range(3)],
-            "qdec": torch.empty(B, H, NQ, D, dtype=torch.bfloat16, device=dev)}
+            "qdec": torch.empty(B, H, NQ, D, dtype=torch.bfloat16, device=dev),
+            "long": [torch.empty(1, 1, NL, D, dtype=torch.bfloat16, device=dev) for _ in range(4)]}
     ws = {"bwd": torch.empty(fa().bwd_workspace_bytes(B, H, N, D), dtype=torch.uint8, device=dev),
           "dec": torch.empty(fa().decode_workspace_bytes(B, H, NQ, N, D), dtype=torch.uint8,
                              device=dev),
           "bwd8": torch.empty(fa().bwd_fp8_workspace_bytes(B, H, N, D), dtype=torch.uint8,
-                              device=dev)}
+                              device=dev),
+          "fsplit": torch.empty(fa().fwd_split_workspace_bytes(1, 1, NL, D, True), dtype=torch.uint8,
+                                device=dev),
+          "bsplit": torch.empty(fa().bwd_split_workspace_bytes(1, 1, NL, D, True), dtype=torch.uint8,
+                                device=dev)}
+    assert ws["fsplit"].numel() > 0  # the split path is the one captured
 
     def refill(seed):
         _fill(bufs, seed)
