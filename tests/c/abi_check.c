@@ -51,6 +51,22 @@ int main(void) {
     fprintf(stderr, "fa_decode_workspace_bytes accepted d = 80\n");
     ++failures;
   }
+  const size_t fsplit = fa_fwd_split_workspace_bytes(1, 1, 16384, 128, 1);
+  if (fsplit == 0 || fa_fwd_split_workspace_bytes(4, 32, 4096, 128, 1) != 0) {
+    fprintf(stderr, "fa_fwd_split_workspace_bytes: %zu\n", fsplit);
+    ++failures;
+  }
+  expect("fa_fwd_split workspace too small",
+         fa_fwd_split(p, p, p, p, f, p, fsplit - 1, 1, 1, 16384, 128, 1, 0.088f, NULL),
+         FA_ERR_WORKSPACE);
+  const size_t bsplit = fa_bwd_split_workspace_bytes(1, 1, 16384, 128, 1);
+  if (bsplit <= fa_bwd_workspace_bytes(1, 1, 16384, 128)) {
+    fprintf(stderr, "fa_bwd_split_workspace_bytes: %zu\n", bsplit);
+    ++failures;
+  }
+  expect("fa_bwd_split workspace too small",
+         fa_bwd_split(p, p, p, p, f, p, p, p, p, p, bsplit - 1, 1, 1, 16384, 128, 1, 0.088f, NULL),
+         FA_ERR_WORKSPACE);
   int cus = 0;
   expect("fa_device_info NULL clock", fa_device_info(0, &cus, NULL), FA_ERR_NULL);
 
