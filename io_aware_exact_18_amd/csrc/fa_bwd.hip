@@ -25,6 +25,9 @@
 //      and dPᵀ = V dOᵀ (each lane owns one query, so LSE_i and D_i are per-lane scalars), forms dSᵀ,
 //      and accumulates dQᵀ += Kᵀ dSᵀ with K read transposed from LDS.
 // Head dimension 96 keeps its tiles in the d = 128 LDS layout (lds_cols in fa_common.h).
+// Split backward (fa_bwd_split, the forward's key-range split rule): the SPLIT instantiations run one
+// segment of the dQ kernel's key tiles or of the dK/dV kernel's query steps and write fp32 partial
+// sums; bwd_split_reduce_kernel adds a row's segments, scales and rounds to bf16.
 // Splitting dQ off costs two recomputed products (7 matrix products executed for the 5 counted) but
 // removes the fp32 atomics a single-kernel dQ would need: measured on MI355X, device-wide fp32 atomic
 // adds sustain about 1.3 TB/s, which for the 4096-token causal workload alone would take ~3 ms.

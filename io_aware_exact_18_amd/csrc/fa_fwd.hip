@@ -35,6 +35,10 @@
 //     the head's K/V stay in that XCD's L2; under the causal mask the heaviest tiles start first.
 //   * Head dimension 256 runs fwd_bf16_split_kernel instead: 8 waves per workgroup, each key tile
 //     split between two waves holding the same queries, merged at the end (see that kernel).
+//   * Key-range split (fa_fwd_split, for grids too small to fill the device; rule in fa_launch.h):
+//     the SPLIT instantiation runs the same loop over one segment of a query tile's key tiles and
+//     writes the segment's unnormalised O, reference maximum and both row sums; fwd_merge_kernel
+//     combines a row's segments (merge_partials in fa_common.h).
 #include "fa_common.h"
 #include "fa_launch.h"
 
