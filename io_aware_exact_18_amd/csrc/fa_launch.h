@@ -128,12 +128,9 @@ inline FwdSplit fwd_split(int B, int H, int N, int d, int causal) {
   const long bh = (long)B * H;
   const long nqt = ((long)N + 127) / 128;
   const long kt = ((long)N + 63) / 64;
-  long total = 0;  // key tiles over every (batch·head, query tile)
-  for (long qt = 0; qt < nqt; ++qt) {
-    const long end = causal ? ((qt + 1) * 128 < (long)N ? (qt + 1) * 128 : (long)N) : (long)N;
-    total += (end + 63) / 64;
-  }
-  total *= bh;
+  // Key tiles over every (batch·head, query tile).  Causal: query tile qt < nqt − 1 ends its keys at
+  // 128(qt + 1), i.e. 2(qt + 1) tiles, and the last one uses all kt, so the sum is (nqt − 1)·nqt + kt.
+  const long total = bh * (causal ? (nqt - 1) * nqt + kt : nqt * kt);
   if (2 * kt * kSlots < 3 * total) return r;
   if (kt * kSlots < 4 * total && kt < 256) return r;
   long seg = kt / 8;
