@@ -74,7 +74,7 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
  *              when that size is 0: the shape is not split and the call is fa_fwd.
  * Split rule: with d ≤ 128, T = the number of 64-key tiles summed over every (batch·head, 128-query
  * tile) pair (under the causal mask a query tile's keys end at its last query) and kt = ⌈N/64⌉, the
- * shape is split when kt·512 ≥ 4·T, or 2·kt·512 ≥ 3·T and kt ≥ 256 (512: two workgroups on each of the
+ * shape is split when 2·kt·512 ≥ 5·T, or 2·kt·512 ≥ 3·T and kt ≥ 256 (512: two workgroups on each of the
  * device's 256 compute units), into segments of seg = min(128, max(16, ⌊kt/8⌋)) tiles, provided seg
  * < kt; nseg = ⌈kt/seg⌉ segments, and the workspace is nseg·B·H·N·(d + 3) fp32 values rounded up to
  * 256 bytes.  Otherwise the workspace is 0.

@@ -108,15 +108,16 @@ inline size_t decode_workspace_bytes(int B, int H, int Nq, int Nk, int d) {
 // sequences): every 128-query tile's key tiles are cut into segments of `seg` 64-key tiles, each
 // (query tile, segment) pair is one workgroup writing a partial result, and a merge kernel combines a
 // row's segments.  nseg = 1 means no split.
-// Rule (measured on MI355X, causal d = 128, 1–8 heads of 4k–64k keys): with T the key tiles summed
-// over all (batch·head, query tile) pairs and kt = ⌈N/64⌉ the longest range, the unsplit grid leaves
-// compute units idle when kt exceeds the average work per workgroup slot, T / kSlots (two workgroups
-// on each of the 256 compute units).  The split is used when kt ≥ 4·T/kSlots, or when kt ≥ 1.5·T/kSlots
-// and rows are long (kt ≥ 256 tiles); below that, the partial results' traffic (d + 3 fp32 values
-// per row and segment, written and read back) and the shorter workgroups cost more than the balance
-// gains (2×4×8192: 739 TFLOP/s unsplit, 564–656 split).  Segments of kt/8 tiles, clamped to 16..128,
-// were within 6% of the best segment length for every shape measured (1×1×16384: 261 → 526 TFLOP/s;
-// 1×1×65536: 861 → 1011).  Head dimension 256 (its own kernel) is not split.
+// Rule (measured on MI355X, causal, d = 64 and 128, 1–8 heads of 4k–64k keys): with T the key tiles
+// summed over all (batch·head, query tile) pairs and kt = ⌈N/64⌉ the longest range, the unsplit grid
+// leaves compute units idle when kt exceeds the average work per workgroup slot, T / kSlots (two
+// workgroups on each of the 256 compute units).  The split is used when kt ≥ 2.5·T/kSlots, or when
+// kt ≥ 1.5·T/kSlots and rows are long (kt ≥ 256 tiles); below that, the partial results' traffic
+// (d + 3 fp32 values per row and segment, written and read back) and the shorter workgroups cost
+// more than the balance gains (2×4×8192, ratio 2: forward 739 TFLOP/s unsplit, 564–656 split).
+// Segments of kt/8 tiles, clamped to 16..128, were within 6% of the best segment length for every
+// shape measured (1×1×16384: 261 → 526 TFLOP/s; 1×1×65536: 861 → 1011).  Head dimension 256 (its own
+// kernel) is not split.
 constexpr long kSlots = 512;
 struct FwdSplit {
   int seg;   // key tiles per segment
@@ -132,7 +133,7 @@ inline FwdSplit fwd_split(int B, int H, int N, int d, int causal) {
   // 128(qt + 1), i.e. 2(qt + 1) tiles, and the last one uses all kt, so the sum is (nqt − 1)·nqt + kt.
   const long total = bh * (causal ? (nqt - 1) * nqt + kt : nqt * kt);
   if (2 * kt * kSlots < 3 * total) return r;
-  if (kt * kSlots < 4 * total && kt < 256) return r;
+  if (2 * kt * kSlots < 5 * total && kt < 256) return r;
   long seg = kt / 8;
   seg = seg < 16 ? 16 : (seg > 128 ? 128 : seg);
   if (seg >= kt) return r;

@@ -106,7 +106,7 @@ def _fwd_split(B, H, N, d, causal):
     """The split rule fa.h documents for fa_fwd_split: (seg, nseg), nseg = 1 when not split."""
     nqt, kt = -(-N // 128), -(-N // 64)
     total = B * H * sum(-(-(min(N, (qt + 1) * 128) if causal else N) // 64) for qt in range(nqt))
-    if d > 128 or 2 * kt * 512 < 3 * total or (kt * 512 < 4 * total and kt < 256):
+    if d > 128 or 2 * kt * 512 < 3 * total or (2 * kt * 512 < 5 * total and kt < 256):
         return 0, 1
     seg = min(128, max(16, kt // 8))
     return (0, 1) if seg >= kt else (seg, -(-kt // seg))
