@@ -112,9 +112,11 @@ __device__ inline float sum_bf16x8(bf16x8 v, float acc) {
 
 // Four fp32 values → four OCP e4m3fn bytes (round to nearest even), first in the lowest byte.  The
 // conversion does not saturate: a magnitude above 464 (the midpoint between 448 and 480) gives the
-// NaN code.  Callers keep their values within ±448.
+// NaN code.  Callers keep their values within ±448.  Each conversion writes one 16-bit half of its
+// result and keeps the other from its third operand; the two calls overwrite both halves, so the
+// first starts from p0's own bits (a register that dies there) rather than from a zeroed one.
 __device__ inline uint32_t pack_e4m3x4(float p0, float p1, float p2, float p3) {
-  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, 0, false);
+  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, __builtin_bit_cast(int, p0), false);
   return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, lo, true);
 }
 

@@ -2,7 +2,7 @@
 // results (not part of libfa.so).  It runs the kernels' own device helpers from fa_common.h over
 // caller-supplied values so the tests can compare them, value by value, with the CPU's rounding:
 //   pack_bf16x2  fp32 → bf16, round to nearest even (every O, dQ, dK, dV element and the bf16 P);
-//   pack_e4m3x4  fp32 → OCP e4m3fn, round to nearest even, saturating (the FP8 forward's P).
+//   pack_e4m3x4  fp32 → OCP e4m3fn, round to nearest even, not saturating (the FP8 forward's P).
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
