@@ -232,11 +232,13 @@ __global__ __launch_bounds__(kThreads, (D == 256 && OUT != 1) ? 1 : 2) void bwd_
       // Element r: query qb + 8(r/4) + 4g + (r%4), key kj.  Masked scores become -inf (P = 0) in a
       // wave-uniform branch taken only by diagonal and ragged tiles.
       if ((kw + 31 >= N) || (CAUSAL && kw + 31 > qb)) {
+        // Masked: kj ≥ N, or (causal) kj > query qb + 4g + c, tested on the element's constant
+        // offset c against one per-lane limit.
+        const bool past_end = kj >= N;
+        const int lim = kj - qb - 4 * g;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int qi = qb + 8 * (r >> 2) + 4 * g + (r & 3);
-          if (kj >= N || (CAUSAL && kj > qi)) sacc[r] = -INFINITY;
-        }
+        for (int r = 0; r < 16; ++r)
+          if (past_end || (CAUSAL && 8 * (r >> 2) + (r & 3) < lim)) sacc[r] = -INFINITY;
       }
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
@@ -465,13 +467,13 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void bwd_dq_kernel(
       // Masked scores become -inf (P = 0) in a wave-uniform branch taken only by diagonal and
       // ragged tiles.
       if ((kv0 + kBC > N) || (CAUSAL && kv0 + kBC - 1 > qw)) {
+        // Masked: key > N − 1 or (causal) key > qi, tested on the element's constant offset c.
+        const int lim = (CAUSAL ? min(N - 1, qi) : N - 1) - kv0 - 4 * g;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = kv0 + 32 * kb + 8 * (r >> 2) + 4 * g + (r & 3);
-            if (key >= N || (CAUSAL && key > qi)) sacc[kb][r] = -INFINITY;
-          }
+          for (int r = 0; r < 16; ++r)
+            if (32 * kb + 8 * (r >> 2) + (r & 3) > lim) sacc[kb][r] = -INFINITY;
       }
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)

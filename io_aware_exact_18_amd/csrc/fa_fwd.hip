@@ -201,13 +201,13 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
       // Accumulator element (kb, r) is key kv0 + 32kb + 8(r/4) + 4g + (r%4) for query qi.  Diagonal
       // and ragged tiles are masked here and their maximum is taken again.
       if ((kv0 + kBC > N) || (CAUSAL && kv0 + kBC - 1 > qw)) {
+        // Masked: key > N − 1 or (causal) key > qi, tested on the element's constant offset c.
+        const int lim = (CAUSAL ? min(N - 1, qi) : N - 1) - kv0 - 4 * g;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = kv0 + 32 * kb + 8 * (r >> 2) + 4 * g + (r & 3);
-            if (key >= N || (CAUSAL && key > qi)) s_cur[kb][r] = -INFINITY;
-          }
+          for (int r = 0; r < 16; ++r)
+            if (32 * kb + 8 * (r >> 2) + (r & 3) > lim) s_cur[kb][r] = -INFINITY;
         mx = rowmax(s_cur);
       }
       const float mt = mx * scale_log2;
@@ -421,11 +421,11 @@ __global__ __launch_bounds__(kSplitThreads, 1) void fwd_bf16_split_kernel(
 #pragma unroll
       for (int s = 0; s < KSTEPS; ++s) sacc = mfma_32x32x16(row_frag<L>(klds, fo, kh, s), qf[s], sacc);
       if ((kb0 + 32 > N) || (CAUSAL && kb0 + 31 > qw)) {
+        // Masked: key > N − 1 or (causal) key > qi, tested on the element's constant offset.
+        const int lim = (CAUSAL ? min(N - 1, qi) : N - 1) - kb0 - 4 * g;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = kb0 + 8 * (r >> 2) + 4 * g + (r & 3);
-          if (key >= N || (CAUSAL && key > qi)) sacc[r] = -INFINITY;
-        }
+        for (int r = 0; r < 16; ++r)
+          if (8 * (r >> 2) + (r & 3) > lim) sacc[r] = -INFINITY;
       }
       float mx = sacc[0];
 #pragma unroll

@@ -210,13 +210,14 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_fp8_kernel(
       // Accumulator element (kb, r), r = 4q + t, is key kv0 + 32kb + 16(q/2) + 8g + 4(q%2) + t.
       const bool need_mask = (kv0 + kBC > N) || (CAUSAL && kv0 + kBC - 1 > qw);
       if (need_mask) {
+        // Masked: key > N − 1 or (causal) key > qi, tested on the element's constant offset.
+        const int lim = (CAUSAL ? min(N - 1, qi) : N - 1) - kv0 - 8 * g;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int q = r >> 2, t = r & 3;
-            const int key = kv0 + 32 * kb + 16 * (q >> 1) + 8 * g + 4 * (q & 1) + t;
-            if (key >= N || (CAUSAL && key > qi)) s_cur[kb][r] = -INFINITY;
+            if (32 * kb + 16 * (q >> 1) + 4 * (q & 1) + t > lim) s_cur[kb][r] = -INFINITY;
           }
       }
       float mx = fmaxf(s_cur[0][0], s_cur[1][0]);
