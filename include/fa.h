@@ -101,6 +101,19 @@ fa_status fa_fwd_fp8(const void* q8, const void* k8, const void* v8,
                      int B, int H, int N, int d, int causal, float softmax_scale, hipStream_t stream);
 
 /*
+ * FP8 forward as fa_fwd_fp8, with the key-range split of fa_fwd_split for shapes with too few query
+ * tiles to fill the device: the same rule, segments and workspace size
+ * (fa_fwd_split_workspace_bytes(B, H, N, d, causal); NULL allowed when that is 0, and then the call
+ * is fa_fwd_fp8).  Each segment's partial output is kept in fp32 with V's descale applied, beside its
+ * reference maximum and the sum of its e4m3-rounded probabilities, and the rows are merged as in
+ * fa_fwd_split.  Errors: as fa_fwd_fp8, plus FA_ERR_WORKSPACE / FA_ERR_ALIGN for the workspace.
+ */
+fa_status fa_fwd_fp8_split(const void* q8, const void* k8, const void* v8, float q_descale,
+                           float k_descale, float v_descale, void* o, float* lse, void* workspace,
+                           size_t workspace_bytes, int B, int H, int N, int d, int causal,
+                           float softmax_scale, hipStream_t stream);
+
+/*
  * Bytes of device workspace fa_bwd needs for a shape: an fp32 [B,H,N] array for D_i = dO_i · O_i,
  * rounded up to 256 bytes.  Returns 0 for an unsupported shape.
  */

@@ -27,7 +27,8 @@ import os
 
 import torch
 
-__all__ = ["fwd", "fwd_split", "fwd_split_workspace_bytes", "fwd_fp8", "bwd", "bwd_split",
+__all__ = ["fwd", "fwd_split", "fwd_split_workspace_bytes", "fwd_fp8", "fwd_fp8_split", "bwd",
+           "bwd_split",
            "bwd_split_workspace_bytes", "bwd_workspace_bytes", "bwd_preprocess", "bwd_dkdv",
            "bwd_dq", "bwd_delta_dq", "bwd_fp8", "bwd_fp8_workspace_bytes", "decode",
            "decode_workspace_bytes",
@@ -67,6 +68,8 @@ def library():
         lib.fa_fwd_split.restype = i
         lib.fa_fwd_fp8.argtypes = [vp, vp, vp, f, f, f, vp, vp, i, i, i, i, i, f, vp]
         lib.fa_fwd_fp8.restype = i
+        lib.fa_fwd_fp8_split.argtypes = [vp, vp, vp, f, f, f, vp, vp, vp, sz, i, i, i, i, i, f, vp]
+        lib.fa_fwd_fp8_split.restype = i
         lib.fa_bwd_workspace_bytes.argtypes = [i, i, i, i]
         lib.fa_bwd_workspace_bytes.restype = sz
         lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, f, vp]
@@ -236,6 +239,32 @@ def fwd_fp8(q8, k8, v8, q_descale, k_descale, v_descale, causal, scale=None):
                                     lse.data_ptr(), B, H, N, d, int(bool(causal)),
                                     _scale(scale, d), _stream(q8.device))
     _check("fa_fwd_fp8", code)
+    return o, lse
+
+
+def fwd_fp8_split(q8, k8, v8, q_descale, k_descale, v_descale, causal, scale=None, workspace=None):
+    """FP8 forward that may split each query tile's key range (fa_fwd_fp8_split): returns (o, lse)
+    as fwd_fp8.  The workspace (uint8, device) is allocated here when not given."""
+    _require(q8, "q8", torch.float8_e4m3fn)
+    if q8.dim() != 4:
+        raise ValueError("q8 must be [B, H, N, d]")
+    _require(k8, "k8", torch.float8_e4m3fn, q8.shape, device=q8.device)
+    _require(v8, "v8", torch.float8_e4m3fn, q8.shape, device=q8.device)
+    B, H, N, d = q8.shape
+    o = torch.empty((B, H, N, d), dtype=torch.bfloat16, device=q8.device)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q8.device)
+    if workspace is None:
+        workspace = torch.empty(max(fwd_split_workspace_bytes(B, H, N, d, causal), 256),
+                                dtype=torch.uint8, device=q8.device)
+    else:
+        _require(workspace, "workspace", torch.uint8, device=q8.device)
+    with torch.cuda.device(q8.device):
+        code = library().fa_fwd_fp8_split(q8.data_ptr(), k8.data_ptr(), v8.data_ptr(),
+                                          float(q_descale), float(k_descale), float(v_descale),
+                                          o.data_ptr(), lse.data_ptr(), workspace.data_ptr(),
+                                          workspace.numel(), B, H, N, d, int(bool(causal)),
+                                          _scale(scale, d), _stream(q8.device))
+    _check("fa_fwd_fp8_split", code)
     return o, lse
 
 

@@ -107,6 +107,28 @@ fa_status fa_fwd_fp8(const void* q8, const void* k8, const void* v8, float q_des
   return fa::launch_fwd_fp8(a, stream) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
+fa_status fa_fwd_fp8_split(const void* q8, const void* k8, const void* v8, float q_descale,
+                           float k_descale, float v_descale, void* o, float* lse, void* workspace,
+                           size_t workspace_bytes, int B, int H, int N, int d, int causal,
+                           float softmax_scale, hipStream_t stream) {
+  if (!q8 || !k8 || !v8 || !o || !lse) return FA_ERR_NULL;
+  fa_status st = check_shape(B, H, N, d, 2);
+  if (st != FA_OK) return st;
+  if (!good_scale(softmax_scale) || !good_scale(q_descale) || !good_scale(k_descale) ||
+      !good_scale(v_descale))
+    return FA_ERR_UNSUPPORTED;
+  if (!aligned(q8, 16) || !aligned(k8, 16) || !aligned(v8, 16) || !aligned(o, 16) ||
+      !aligned(lse, 16))
+    return FA_ERR_ALIGN;
+  const size_t need = fa::fwd_split_workspace_bytes(B, H, N, d, causal ? 1 : 0);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return FA_ERR_WORKSPACE;
+  if (need > 0 && !aligned(workspace, 256)) return FA_ERR_ALIGN;
+  fa::Fp8FwdArgs a{q8, k8, v8, q_descale, k_descale, v_descale, o, lse,
+                   B, H, N, d, causal ? 1 : 0, softmax_scale};
+  a.workspace = need > 0 ? workspace : nullptr;
+  return fa::launch_fwd_fp8(a, stream) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
 size_t fa_bwd_workspace_bytes(int B, int H, int N, int d) {
   if (check_shape(B, H, N, d, 2) != FA_OK) return 0;
   return fa::bwd_delta_bytes(B, H, N);

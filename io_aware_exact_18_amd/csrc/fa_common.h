@@ -265,6 +265,15 @@ __device__ inline void vec64_to_lds(__amdgpu_buffer_rsrc_t r, int e0, float* lds
                                            (uint32_t)(e0 + lane) * 4u, 0, 0, 0);
 }
 
+// Partial-result outputs of the forwards' key-range split (fwd_split in fa_launch.h): per (segment,
+// batch·head, query) row the unnormalised output (D fp32, in units of the output) and (m, l, lr).
+struct SplitOut {
+  float* part_o;   // [nseg][B·H][N][D]
+  float* part_ml;  // [nseg][B·H][N][3]: reference maximum (base 2), fp32 and bf16-rounded row sums
+  int seg;         // key tiles per segment
+  int bh_count;    // B·H
+};
+
 // Combines `nseg` partial results of one query row, each over a disjoint range of keys, into the row's
 // output and logsumexp: the online-softmax recurrence of "Anatomy of a FlashAttention Kernel", section
 // "What is online softmax and how does tiling keep it exact?", applied to whole key ranges.  Partial s

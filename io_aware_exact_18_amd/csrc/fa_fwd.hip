@@ -83,14 +83,6 @@ __device__ inline void scores_tile(const char* klds, const FragOffsets<lds_cols<
   for (int i = 0; i < 2 * NS; ++i) acc[i & 1] = mfma_32x32x16(f[i], qf[i >> 1], acc[i & 1]);
 }
 
-// Partial-result outputs of the key-range split (fwd_split in fa_launch.h).
-struct SplitOut {
-  float* part_o;   // [nseg][B·H][N][D]: unnormalised output of the segment's keys
-  float* part_ml;  // [nseg][B·H][N][3]: reference maximum (base 2), fp32 and bf16-rounded row sums
-  int seg;         // key tiles per segment
-  int bh_count;    // B·H
-};
-
 template <int D, bool CAUSAL, bool SPLIT>
 __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
@@ -561,10 +553,8 @@ hipError_t launch(const FwdArgs& a, hipStream_t stream) {
                        nqt, scale_log2, 0, so);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((fwd_merge_kernel<D, CAUSAL>), dim3(bh * (uint32_t)a.N), dim3(64), 0, stream,
-                       (const float*)so.part_o, (const float*)so.part_ml, (bf16*)a.o, a.lse, a.N,
-                       (int)bh, sp.seg);
-    return hipGetLastError();
+    return launch_fwd_merge(so.part_o, so.part_ml, a.o, a.lse, (int)bh, a.N, D, CAUSAL ? 1 : 0,
+                            sp.seg, stream);
   }
   const uint32_t total = bh * nqt;
   const int remap = use_xcd_order(total, (long)bh, CAUSAL ? 1 : 0);
@@ -575,6 +565,30 @@ hipError_t launch(const FwdArgs& a, hipStream_t stream) {
 }
 
 }  // namespace
+
+namespace {
+template <int D, bool CAUSAL>
+hipError_t merge_rows(const float* part_o, const float* part_ml, void* o, float* lse, int bh, int N,
+                      int seg, hipStream_t stream) {
+  hipLaunchKernelGGL((fwd_merge_kernel<D, CAUSAL>), dim3((uint32_t)bh * (uint32_t)N), dim3(64), 0,
+                     stream, part_o, part_ml, (bf16*)o, lse, N, bh, seg);
+  return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_fwd_merge(const float* part_o, const float* part_ml, void* o, float* lse, int bh,
+                            int N, int d, int causal, int seg, hipStream_t stream) {
+  if (d == 64)
+    return causal ? merge_rows<64, true>(part_o, part_ml, o, lse, bh, N, seg, stream)
+                  : merge_rows<64, false>(part_o, part_ml, o, lse, bh, N, seg, stream);
+  if (d == 96)
+    return causal ? merge_rows<96, true>(part_o, part_ml, o, lse, bh, N, seg, stream)
+                  : merge_rows<96, false>(part_o, part_ml, o, lse, bh, N, seg, stream);
+  if (d == 128)
+    return causal ? merge_rows<128, true>(part_o, part_ml, o, lse, bh, N, seg, stream)
+                  : merge_rows<128, false>(part_o, part_ml, o, lse, bh, N, seg, stream);
+  return hipErrorInvalidValue;
+}
 
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream) {
   if (a.d == 64) return a.causal ? launch<64, true>(a, stream) : launch<64, false>(a, stream);

@@ -81,11 +81,12 @@ __device__ inline u32x2 lds_read_tr8(const uint8_t* p) {
   return __builtin_bit_cast(u32x2, r);
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool SPLIT>
 __global__ __launch_bounds__(kThreads, 2) void fwd_fp8_kernel(
     const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K, const uint8_t* __restrict__ V,
     bf16* __restrict__ O, float* __restrict__ LSE, int N, int nqt, float c_log2, float v_descale,
-    int remap) {
+    int remap, SplitOut so) {
+  static_assert(!SPLIT || col_splits<D>() == 1, "the key-range split runs d ≤ 128");
   static_assert(D == 64 || D == 96 || D == 128 || D == 256, "head dims of the fp8 forward");
   constexpr int LR = lds_row<D>();
   constexpr int KS = LR / 64;                   // k-steps of Sᵀ
@@ -101,7 +102,13 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_fp8_kernel(
   const int g = lane >> 5;
   const int lc = lane & 31;
 
-  const uint32_t logical = remap ? xcd_remap(blockIdx.x, gridDim.x) : blockIdx.x;
+  uint32_t logical = remap ? xcd_remap(blockIdx.x, gridDim.x) : blockIdx.x;
+  int sg = 0;  // key segment (split only): work items are segment-major
+  if constexpr (SPLIT) {
+    const uint32_t per_seg = (uint32_t)so.bh_count * (uint32_t)nqt;
+    sg = (int)(logical / per_seg);
+    logical %= per_seg;
+  }
   const int half = col_splits<D>() == 2 ? (int)(logical & 1u) : 0;  // column half of O (d = 256)
   const uint32_t item = col_splits<D>() == 2 ? logical >> 1 : logical;
   const int bh = item / nqt;
@@ -110,6 +117,13 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_fp8_kernel(
   const int q0 = qt * kBR;
   const int qw = q0 + 32 * wave;
   const int qi = qw + lc;
+
+  const int kv_end = CAUSAL ? min(N, q0 + kBR) : N;
+  const int ntiles = (kv_end + kBC - 1) / kBC;
+  // Key tiles [t_beg, t_end) of this workgroup: all of them, or one segment of the split.
+  const int t_beg = SPLIT ? sg * so.seg : 0;
+  const int t_end = SPLIT ? min(ntiles, t_beg + so.seg) : ntiles;
+  if (SPLIT && t_beg >= t_end) return;  // the query tile's keys end before this segment
 
   const size_t head = (size_t)bh * N * D;
   const uint32_t head_bytes = (uint32_t)N * D;
@@ -154,13 +168,11 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_fp8_kernel(
       voff[db] = (uint32_t)(r * LR + 16 * ((2 * (db + DB * half) + u) ^ swz8<LR>(r)) + 8 * b);
   }
 
-  const int kv_end = CAUSAL ? min(N, q0 + kBR) : N;
-  const int ntiles = (kv_end + kBC - 1) / kBC;
-  const int wave_tiles = CAUSAL ? min(ntiles, (qw + 31) / kBC + 1) : ntiles;
+  const int wave_tiles = CAUSAL ? min(t_end, (qw + 31) / kBC + 1) : t_end;
 
-  copy(mk, 0, k0s);
-  if (ntiles > 1) copy(mk, kBC, k1s);
-  copy(mv, 0, v0s);
+  copy(mk, t_beg * kBC, k0s);
+  if (t_beg + 1 < t_end) copy(mk, (t_beg + 1) * kBC, k1s);
+  copy(mv, t_beg * kBC, v0s);
   wait_vmem_all();
   __syncthreads();
 
@@ -203,8 +215,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_fp8_kernel(
     uint8_t* const k_next = P ? k0s : k1s;
     uint8_t* const v_this = P ? v1s : v0s;
     uint8_t* const v_next = P ? v0s : v1s;
-    if (j + 2 < ntiles) copy(mk, (j + 2) * kBC, k_this);
-    if (j + 1 < ntiles) copy(mv, (j + 1) * kBC, v_next);
+    if (j + 2 < t_end) copy(mk, (j + 2) * kBC, k_this);
+    if (j + 1 < t_end) copy(mv, (j + 1) * kBC, v_next);
     const int kv0 = j * kBC;
     if (j < wave_tiles) {
       // Accumulator element (kb, r), r = 4q + t, is key kv0 + 32kb + 16(q/2) + 8g + 4(q%2) + t.
@@ -277,9 +289,32 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_fp8_kernel(
     __syncthreads();
   };
 
-  for (int j = 0; j < ntiles; j += 2) {
+  for (int j = t_beg; j < t_end; j += 2) {
     tile(std::integral_constant<int, 0>{}, j);
-    if (j + 1 < ntiles) tile(std::integral_constant<int, 1>{}, j + 1);
+    if (j + 1 < t_end) tile(std::integral_constant<int, 1>{}, j + 1);
+  }
+
+  if constexpr (SPLIT) {
+    // The segment's partial result in the units of O (V's descale applied), its reference maximum
+    // (the 2^kPExp offset of P removed) and the sum of the rounded P, which serves as both row sums.
+    if (qi < N) {
+      const size_t row = ((size_t)sg * so.bh_count + bh) * N + qi;
+      float* orow = so.part_o + row * D;
+#pragma unroll
+      for (int b = 0; b < DB; ++b)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const f32x4 w = {oacc[b][4 * r4] * v_descale, oacc[b][4 * r4 + 1] * v_descale,
+                           oacc[b][4 * r4 + 2] * v_descale, oacc[b][4 * r4 + 3] * v_descale};
+          *(f32x4*)&orow[32 * b + 8 * r4 + 4 * g] = w;
+        }
+      if (g == 0) {
+        so.part_ml[3 * row] = m - kPExp;
+        so.part_ml[3 * row + 1] = lacc[0];
+        so.part_ml[3 * row + 2] = lacc[0];
+      }
+    }
+    return;
   }
 
   const float l = lacc[0];
@@ -302,12 +337,29 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_fp8_kernel(
 template <int D, bool CAUSAL>
 hipError_t launch(const Fp8FwdArgs& a, hipStream_t stream) {
   const int nqt = (a.N + kBR - 1) / kBR;
-  const uint32_t total = (uint32_t)a.B * a.H * nqt * col_splits<D>();
-  const int remap = use_xcd_order(total, (long)a.B * a.H, CAUSAL ? 1 : 0);
   const float c_log2 = a.scale * a.q_descale * a.k_descale * kLog2e;
-  hipLaunchKernelGGL((fwd_fp8_kernel<D, CAUSAL>), dim3(total), dim3(kThreads), 0, stream,
+  const uint32_t bh = (uint32_t)a.B * a.H;
+  if constexpr (col_splits<D>() == 1) {
+    // Key-range split (the bf16 forward's rule and merge; fwd_split in fa_launch.h).
+    const FwdSplit sp = a.workspace ? fwd_split(a.B, a.H, a.N, D, CAUSAL ? 1 : 0) : FwdSplit{0, 1};
+    if (sp.nseg > 1) {
+      SplitOut so{(float*)a.workspace, nullptr, sp.seg, (int)bh};
+      so.part_ml = so.part_o + (size_t)sp.nseg * bh * a.N * D;
+      hipLaunchKernelGGL((fwd_fp8_kernel<D, CAUSAL, true>), dim3((uint32_t)sp.nseg * bh * nqt),
+                         dim3(kThreads), 0, stream, (const uint8_t*)a.q8, (const uint8_t*)a.k8,
+                         (const uint8_t*)a.v8, (bf16*)a.o, a.lse, a.N, nqt, c_log2, a.v_descale, 0,
+                         so);
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      return launch_fwd_merge(so.part_o, so.part_ml, a.o, a.lse, (int)bh, a.N, D, CAUSAL ? 1 : 0,
+                              sp.seg, stream);
+    }
+  }
+  const uint32_t total = bh * nqt * col_splits<D>();
+  const int remap = use_xcd_order(total, (long)bh, CAUSAL ? 1 : 0);
+  hipLaunchKernelGGL((fwd_fp8_kernel<D, CAUSAL, false>), dim3(total), dim3(kThreads), 0, stream,
                      (const uint8_t*)a.q8, (const uint8_t*)a.k8, (const uint8_t*)a.v8, (bf16*)a.o,
-                     a.lse, a.N, nqt, c_log2, a.v_descale, remap);
+                     a.lse, a.N, nqt, c_log2, a.v_descale, remap, SplitOut{nullptr, nullptr, 0, 0});
   return hipGetLastError();
 }
 

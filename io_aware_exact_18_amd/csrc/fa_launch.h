@@ -26,6 +26,7 @@ struct Fp8FwdArgs {
   float* lse;
   int B, H, N, d, causal;
   float scale;
+  void* workspace = nullptr;  // fwd_split_workspace_bytes bytes: allows the key-range split
 };
 
 struct BwdArgs {
@@ -170,6 +171,10 @@ inline size_t bwd_split_part_bytes(int nseg, int B, int H, int N, int d) {
 }
 
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream);
+// Key-range split, second step (both forwards): one wave per (batch·head, query) row combines the row's
+// segments (as many as its query tile's key range spans) into O (bf16) and LSE; d ≤ 128.
+hipError_t launch_fwd_merge(const float* part_o, const float* part_ml, void* o, float* lse, int bh,
+                            int N, int d, int causal, int seg, hipStream_t stream);
 hipError_t launch_fwd_fp8(const Fp8FwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd_pre(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t stream);

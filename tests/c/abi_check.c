@@ -59,6 +59,9 @@ int main(void) {
   expect("fa_fwd_split workspace too small",
          fa_fwd_split(p, p, p, p, f, p, fsplit - 1, 1, 1, 16384, 128, 1, 0.088f, NULL),
          FA_ERR_WORKSPACE);
+  expect("fa_fwd_fp8_split workspace NULL",
+         fa_fwd_fp8_split(p, p, p, 1.f, 1.f, 1.f, p, f, NULL, 0, 1, 1, 16384, 128, 1, 0.088f, NULL),
+         FA_ERR_WORKSPACE);
   const size_t bsplit = fa_bwd_split_workspace_bytes(1, 1, 16384, 128, 1);
   if (bsplit <= fa_bwd_workspace_bytes(1, 1, 16384, 128)) {
     fprintf(stderr, "fa_bwd_split_workspace_bytes: %zu\n", bsplit);

@@ -30,6 +30,7 @@ def lib():
     lib.fa_bwd_split_workspace_bytes.restype = sz
     lib.fa_bwd_split.argtypes = [vp] * 10 + [sz, i, i, i, i, i, f, vp]
     lib.fa_fwd_fp8.argtypes = [vp, vp, vp, f, f, f, vp, vp, i, i, i, i, i, f, vp]
+    lib.fa_fwd_fp8_split.argtypes = [vp, vp, vp, f, f, f, vp, vp, vp, sz, i, i, i, i, i, f, vp]
     lib.fa_bwd_workspace_bytes.argtypes = [i, i, i, i]
     lib.fa_bwd_workspace_bytes.restype = sz
     lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, f, vp]
@@ -52,7 +53,7 @@ def test_exports_match_header(lib):
     text = open(HEADER).read()
     declared = set(re.findall(r"^\s*(?:fa_status|size_t|const char\*)\s+(fa_\w+)\s*\(", text, re.M))
     assert declared == {"fa_fwd", "fa_fwd_split", "fa_fwd_split_workspace_bytes", "fa_bwd_split",
-                        "fa_bwd_split_workspace_bytes", "fa_fwd_fp8", "fa_bwd_workspace_bytes", "fa_bwd", "fa_status_str",
+                        "fa_bwd_split_workspace_bytes", "fa_fwd_fp8", "fa_fwd_fp8_split", "fa_bwd_workspace_bytes", "fa_bwd", "fa_status_str",
                         "fa_bwd_preprocess", "fa_bwd_dkdv", "fa_bwd_dq", "fa_device_info",
                         "fa_decode", "fa_decode_workspace_bytes", "fa_bwd_fp8",
                         "fa_bwd_fp8_workspace_bytes", "fa_bwd_noalloc", "fa_bwd_noalloc_max_rows",
@@ -192,6 +193,21 @@ def test_bwd_split_rejections(lib):
     assert need > lib.fa_bwd_workspace_bytes(1, 1, 16384, 128)  # the split's partial sums
     assert bwd_split(lib, ws_bytes=need - 1) == WORKSPACE
     assert bwd_split(lib, ws=P + 16) == ALIGN
+
+
+def test_fwd_fp8_split_rejections(lib):
+    def call(q=P, v_descale=0.5, ws=P, ws_bytes=1 << 34, N=16384, d=128):
+        return lib.fa_fwd_fp8_split(q, P, P, 0.5, 0.5, v_descale, P, P, ws, ws_bytes, 1, 1, N, d, 1,
+                                    0.125, None)
+    assert call(q=None) == NULL
+    assert call(N=0) == SHAPE
+    assert call(d=80) == UNSUP
+    assert call(v_descale=0.0) == UNSUP
+    assert call(q=MIS) == ALIGN
+    need = lib.fa_fwd_split_workspace_bytes(1, 1, 16384, 128, 1)
+    assert call(ws=None) == WORKSPACE
+    assert call(ws_bytes=need - 1) == WORKSPACE
+    assert call(ws=P + 16) == ALIGN
 
 
 def test_fwd_fp8_rejections(lib):

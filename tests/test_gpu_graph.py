@@ -1,9 +1,9 @@
 """The library under HIP graph capture.  Every entry point (forward, backward, decoding, the FP8
-forward and backward, and the split forward and backward on a shape they split) is captured into one
-graph through the current stream and replayed.  The
-kernels are deterministic, so each replay must reproduce the eager results bit for bit, also with
-eager work between replays and after the captured input tensors are refilled in place.  One head of
-the replayed results is also checked against the fp64 oracle.
+forward and backward, and the split forward, backward and FP8 forward on a shape they split) is
+captured into one graph through the current stream and replayed.  The kernels are deterministic, so
+each replay must reproduce the eager results bit for bit, also with eager work between replays and
+after the captured input tensors are refilled in place.  One head of the replayed results is also
+checked against the fp64 oracle.
 """
 
 import math
@@ -41,7 +41,7 @@ def _fill(bufs, seed):
     g = torch.Generator().manual_seed(seed)
     for t in bufs["bf16"] + bufs["long"]:
         t.copy_(torch.randn(t.shape, generator=g).to(torch.bfloat16))
-    for t in bufs["e4m3"]:  # e4m3 codes spread over most of the format's range
+    for t in bufs["e4m3"] + bufs["long8"]:  # e4m3 codes spread over most of the format's range
         t.copy_((torch.randn(t.shape, generator=g) * 100.0).clamp(-448.0, 448.0)
                 .to(torch.float8_e4m3fn))
 
@@ -59,7 +59,8 @@ def _work(bufs, ws):
     ql, kl, vl, dol = bufs["long"]
     os_, ls_ = fa().fwd_split(ql, kl, vl, True, SCALE, workspace=ws["fsplit"])
     gs = fa().bwd_split(ql, kl, vl, os_, ls_, dol, True, SCALE, workspace=ws["bsplit"])
-    return [o, lse, dq, dk, dv, od, ld, o8, l8, *g8, os_, ls_, *gs]
+    o8s, l8s = fa().fwd_fp8_split(*bufs["long8"], *S8, True, SCALE, workspace=ws["fsplit8"])
+    return [o, lse, dq, dk, dv, od, ld, o8, l8, *g8, os_, ls_, *gs, o8s, l8s]
 
 
 def test_graph_capture_and_replay_match_eager():
@@ -68,7 +69,9 @@ def test_graph_capture_and_replay_match_eager():
             "e4m3": [torch.empty(B, H, N, D, dtype=torch.float8_e4m3fn, device=dev)
                      for _ in range(3)],
             "qdec": torch.empty(B, H, NQ, D, dtype=torch.bfloat16, device=dev),
-            "long": [torch.empty(1, 1, NL, D, dtype=torch.bfloat16, device=dev) for _ in range(4)]}
+            "long": [torch.empty(1, 1, NL, D, dtype=torch.bfloat16, device=dev) for _ in range(4)],
+            "long8": [torch.empty(1, 1, NL, D, dtype=torch.float8_e4m3fn, device=dev)
+                      for _ in range(3)]}
     ws = {"bwd": torch.empty(fa().bwd_workspace_bytes(B, H, N, D), dtype=torch.uint8, device=dev),
           "dec": torch.empty(fa().decode_workspace_bytes(B, H, NQ, N, D), dtype=torch.uint8,
                              device=dev),
@@ -77,7 +80,9 @@ def test_graph_capture_and_replay_match_eager():
           "fsplit": torch.empty(fa().fwd_split_workspace_bytes(1, 1, NL, D, True), dtype=torch.uint8,
                                 device=dev),
           "bsplit": torch.empty(fa().bwd_split_workspace_bytes(1, 1, NL, D, True), dtype=torch.uint8,
-                                device=dev)}
+                                device=dev),
+          "fsplit8": torch.empty(fa().fwd_split_workspace_bytes(1, 1, NL, D, True), dtype=torch.uint8,
+                                 device=dev)}
     assert ws["fsplit"].numel() > 0  # the split path is the one captured
 
     def refill(seed):

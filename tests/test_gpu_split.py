@@ -1,5 +1,5 @@
-"""GPU parity of the key-range split forward (fa_fwd_split) against the fp64 CPU oracle, and against
-the unsplit forward.
+"""GPU parity of the key-range split forward, backward and FP8 forward (fa_fwd_split, fa_bwd_split,
+fa_fwd_fp8_split) against the fp64 CPU oracle, and against the unsplit calls.
 
 The split only changes how a query tile's keys are grouped: each segment's partial result is merged
 by its softmax mass, so the bounds are those of the forward (O max-abs ≤ 1e-2, LSE max-abs ≤ 1e-3),
@@ -13,6 +13,7 @@ import pytest
 import torch
 
 import oracle
+import workloads
 
 pytestmark = pytest.mark.gpu
 
@@ -272,3 +273,89 @@ def test_bwd_split_workspace_reuse_with_smaller_shape():
     split, plain = _bwd_both(q.cuda(), k.cuda(), v.cuda(), do.cuda(), True, 0.125, workspace=ws)
     _check_bwd_oracle(q, k, v, do, split, True, 0.125)
     _check_same(split, plain)
+
+
+# ------------------------------------------------------------------------------------------------
+# Split FP8 forward (fa_fwd_fp8_split): the FP8 forward's bounds against the oracle on the values the
+# e4m3 codes stand for (O max-abs ≤ 6e-2, LSE max-abs ≤ 5e-2, as in the fixed-shape FP8 tests).
+
+FP8_O_TOL, FP8_LSE_TOL = 6e-2, 5e-2
+
+
+def _fp8_inputs(B, H, N, d, seed):
+    g = torch.Generator().manual_seed(seed)
+    out = {}
+    for name in ("q", "k", "v"):
+        out[name + "8"], out["s" + name] = workloads.quantize_e4m3(torch.randn(B, H, N, d, generator=g))
+    return out
+
+
+def _check_fp8_rows(inp, o, lse, causal, scale, rows=None):
+    q, k, v = (workloads.dequantized64(inp[n + "8"], inp["s" + n]) for n in ("q", "k", "v"))
+    B, H, N, d = q.shape
+    worst_o = worst_l = 0.0
+    for h in range(B * H):
+        b, hh = divmod(h, H)
+        o_c, l_c = o[b, hh].cpu(), lse[b, hh].cpu()
+        for r0, r1 in (rows or [(0, N)]):
+            kend = r1 if causal else N
+            o_ref, l_ref = oracle.attention_head_fwd64(q[b, hh, r0:r1].numpy(), k[b, hh, :kend].numpy(),
+                                                      v[b, hh, :kend].numpy(), causal, scale,
+                                                      q_offset=r0)
+            e_o = float(np.abs(_np64(o_c[r0:r1]) - o_ref).max())
+            e_l = float(np.abs(_np64(l_c[r0:r1]) - l_ref).max())
+            assert e_o <= FP8_O_TOL and e_l <= FP8_LSE_TOL, (h, r0, e_o, e_l)
+            worst_o, worst_l = max(worst_o, e_o), max(worst_l, e_l)
+    return worst_o, worst_l
+
+
+def _run_fp8(fn, inp, causal, scale):
+    o, lse = fn(*(inp[n + "8"].cuda() for n in ("q", "k", "v")), inp["sq"], inp["sk"], inp["sv"],
+                causal, scale)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+SPLIT_FP8 = [(1, 1, n, d, c) for d in (64, 96, 128) for c in (False, True) for n in (1025, 3001)]
+
+
+@pytest.mark.parametrize("B,H,N,d,causal", SPLIT_FP8)
+def test_fwd_fp8_split_small(B, H, N, d, causal):
+    assert fa().fwd_split_workspace_bytes(B, H, N, d, causal) > 0
+    inp = _fp8_inputs(B, H, N, d, seed=11 * N + d + int(causal))
+    scale = 1.0 / math.sqrt(d)
+    o, lse = _run_fp8(fa().fwd_fp8_split, inp, causal, scale)
+    worst = _check_fp8_rows(inp, o, lse, causal, scale)
+    o_u, l_u = _run_fp8(fa().fwd_fp8, inp, causal, scale)
+    d_o = float((o.float() - o_u.float()).abs().max())
+    assert d_o <= FP8_O_TOL
+    print(f"PARITY fwd_fp8_split {B}x{H}x{N}x{d} causal={causal}: O {worst[0]:.3g} "
+          f"LSE {worst[1]:.3g}; vs unsplit O {d_o:.3g}")
+
+
+def test_fwd_fp8_split_long_head():
+    """One causal head of 16384 keys: split against unsplit FP8 outputs (within the FP8 bounds), row
+    blocks against the oracle, bit-identical repeated calls."""
+    B, H, N, d, causal = 1, 1, 16384, 128, True
+    inp = _fp8_inputs(B, H, N, d, seed=16384 * 3)
+    scale = 1.0 / math.sqrt(d)
+    o, lse = _run_fp8(fa().fwd_fp8_split, inp, causal, scale)
+    o2, l2 = _run_fp8(fa().fwd_fp8_split, inp, causal, scale)
+    assert torch.equal(o, o2) and torch.equal(l2, lse)
+    o_u, l_u = _run_fp8(fa().fwd_fp8, inp, causal, scale)
+    assert float((o.float() - o_u.float()).abs().max()) <= FP8_O_TOL
+    # each segment rounds P to e4m3 against its own reference maximum, so the sums differ at the
+    # level of that rounding; both are held to the oracle bound below
+    assert float((lse - l_u).abs().max()) <= FP8_LSE_TOL
+    worst = _check_fp8_rows(inp, o, lse, causal, scale,
+                            rows=[(0, 8), (N // 2 - 4, N // 2 + 4), (N - 8, N)])
+    print(f"PARITY fwd_fp8_split 1x1x{N}x{d} causal: O {worst[0]:.3g} LSE {worst[1]:.3g}")
+
+
+def test_fwd_fp8_split_unsplit_shapes_equal_fwd_fp8():
+    for B, H, N, d in ((4, 8, 2048, 128), (1, 1, 1024, 64), (1, 1, 3000, 256)):
+        assert fa().fwd_split_workspace_bytes(B, H, N, d, True) == 0
+        inp = _fp8_inputs(B, H, N, d, seed=B * H + N)
+        a = _run_fp8(fa().fwd_fp8, inp, True, 1.0 / math.sqrt(d))
+        b = _run_fp8(fa().fwd_fp8_split, inp, True, 1.0 / math.sqrt(d))
+        assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1]), (B, H, N, d)
