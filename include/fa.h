@@ -67,17 +67,17 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
  * result (unnormalised output, reference maximum, row sums) goes to the workspace and a second kernel
  * combines a row's segments by their softmax mass: the recurrence of "Anatomy of a FlashAttention
  * Kernel", section "What is online softmax and how does tiling keep it exact?", applied to whole key
- * ranges.  The result is the same attention; it can differ from fa_fwd's in the last bits (another
- * summation order).
+ * ranges.  The result is the same attention, within rounding of fa_fwd's: each segment rounds its
+ * probabilities to bf16 against its own reference maximum, and the sums run in another order.
  *   workspace  device memory of at least fa_fwd_split_workspace_bytes(B, H, N, d, causal) bytes,
  *              256-byte aligned, owned by the caller, contents undefined after the call.  May be NULL
  *              when that size is 0: the shape is not split and the call is fa_fwd.
  * Split rule: with d ≤ 128, T = the number of 64-key tiles summed over every (batch·head, 128-query
  * tile) pair (under the causal mask a query tile's keys end at its last query) and kt = ⌈N/64⌉, the
- * shape is split when 2·kt·512 ≥ 5·T, or 2·kt·512 ≥ 3·T and kt ≥ 256 (512: two workgroups on each of the
- * device's 256 compute units), into segments of seg = min(128, max(16, ⌊kt/8⌋)) tiles, provided seg
- * < kt; nseg = ⌈kt/seg⌉ segments, and the workspace is nseg·B·H·N·(d + 3) fp32 values rounded up to
- * 256 bytes.  Otherwise the workspace is 0.
+ * shape is split when 2·kt·512 ≥ 5·T, or 2·kt·512 ≥ 3·T and kt ≥ 256 (512: two workgroups on each
+ * of the device's 256 compute units), into segments of seg = min(128, max(16, ⌊kt/8⌋)) tiles,
+ * provided seg < kt; nseg = ⌈kt/seg⌉ segments, and the workspace is nseg·B·H·N·(d + 3) fp32 values
+ * rounded up to 256 bytes.  Otherwise the workspace is 0.
  * Errors: as fa_fwd; FA_ERR_WORKSPACE when the workspace is needed and NULL or too small,
  * FA_ERR_ALIGN when it is not 256-byte aligned.  Head dimension 256 is never split.
  */
@@ -106,7 +106,9 @@ fa_status fa_fwd_fp8(const void* q8, const void* k8, const void* v8,
  * (fa_fwd_split_workspace_bytes(B, H, N, d, causal); NULL allowed when that is 0, and then the call
  * is fa_fwd_fp8).  Each segment's partial output is kept in fp32 with V's descale applied, beside its
  * reference maximum and the sum of its e4m3-rounded probabilities, and the rows are merged as in
- * fa_fwd_split.  Errors: as fa_fwd_fp8, plus FA_ERR_WORKSPACE / FA_ERR_ALIGN for the workspace.
+ * fa_fwd_split; each segment rounds P to e4m3 against its own reference maximum, so the result is
+ * fa_fwd_fp8's within that rounding.  Errors: as fa_fwd_fp8, plus FA_ERR_WORKSPACE / FA_ERR_ALIGN
+ * for the workspace.
  */
 fa_status fa_fwd_fp8_split(const void* q8, const void* k8, const void* v8, float q_descale,
                            float k_descale, float v_descale, void* o, float* lse, void* workspace,
@@ -173,7 +175,8 @@ fa_status fa_bwd_delta_dq(const void* q, const void* k, const void* v, const voi
  * fp32 partial sums of its gradients to the workspace and a last kernel adds a row's segments, applies
  * the scale and rounds to bf16 (the gradients of "Anatomy of a FlashAttention Kernel", section "How
  * does FlashAttention save memory in the backward pass?", summed over key or query ranges in another
- * grouping).  Results can differ from fa_bwd's in the last bits.
+ * grouping).  Each probability is recomputed exactly as fa_bwd does; only the order of the
+ * gradient sums differs, so results can differ from fa_bwd's in the last bits.
  *   workspace  at least fa_bwd_split_workspace_bytes(B, H, N, d, causal) bytes, 256-byte aligned,
  *              owned by the caller, contents undefined after the call: −D_i (as fa_bwd), then, when
  *              split, nseg_q·B·H·N·d fp32 partial dQ sums and nseg_k·B·H·N·d each for dK and dV,
