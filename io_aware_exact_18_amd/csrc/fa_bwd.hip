@@ -131,8 +131,8 @@ __global__ __launch_bounds__(kThreads, (D == 256 && OUT != 1) ? 1 : 2) void bwd_
     sg = (int)(logical / per_seg);
     logical %= per_seg;
   }
-  const int bh = logical / nkt;
-  const int kt = logical % nkt;
+  int bh, kt;  // key blocks in order, heaviest first under the causal mask
+  head_tile(logical, nkt, SPLIT ? so.bh_count : (int)(gridDim.x / nkt), bh, kt);
   const int k0 = kt * kBKV;
   const int kw = k0 + 32 * wave;  // first key of this wave
   const int kj = kw + lc;         // this lane's key (column of the score tiles)
@@ -360,8 +360,8 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void bwd_dq_kernel(
     sg = (int)(logical / per_seg);
     logical %= per_seg;
   }
-  const int bh = logical / nqt;
-  int qt = logical % nqt;
+  int bh, qt;
+  head_tile(logical, nqt, SPLIT ? so.bh_count : (int)(gridDim.x / nqt), bh, qt);
   if (CAUSAL) qt = nqt - 1 - qt;  // heaviest tiles first
   const int q0 = qt * kBR;
   const int qw = q0 + 32 * wave;

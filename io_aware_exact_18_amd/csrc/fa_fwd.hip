@@ -31,8 +31,9 @@
 //     then an exactly normalised average of V rows under the rounded weights: in a row dominated by
 //     one key it returns that key's V row however p rounds, where dividing by l would leave p's
 //     rounding error (up to 2^-9 of |V|) in O.
-//   * Grid: one workgroup per (batch·head, query tile); query tiles of one head are kept on one XCD so
-//     the head's K/V stay in that XCD's L2; under the causal mask the heaviest tiles start first.
+//   * Grid: one workgroup per (batch·head, query tile); the query tiles of a group of four heads are
+//     kept on one XCD so the heads' K/V stay in that XCD's L2, interleaved head by head so that under
+//     the causal mask every group's heaviest tiles start first (head_tile in fa_common.h).
 //   * Head dimension 256 runs fwd_bf16_split_kernel instead: 8 waves per workgroup, each key tile
 //     split between two waves holding the same queries, merged at the end (see that kernel).
 //   * Key-range split (fa_fwd_split, for grids too small to fill the device; rule in fa_launch.h):
@@ -114,8 +115,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     sg = (int)(logical / per_seg);
     logical %= per_seg;
   }
-  const int bh = logical / nqt;
-  int qt = logical % nqt;
+  int bh, qt;  // tile order: heaviest first under the causal mask
+  head_tile(logical, nqt, SPLIT ? so.bh_count : (int)(total / nqt), bh, qt);
   if (CAUSAL) qt = nqt - 1 - qt;
   const int q0 = qt * kBR;
   const int qw = q0 + wave * 32;  // first query of this wave
@@ -359,8 +360,8 @@ __global__ __launch_bounds__(kSplitThreads, 1) void fwd_bf16_split_kernel(
 
   const uint32_t total = gridDim.x;
   const uint32_t logical = remap ? xcd_remap(blockIdx.x, total) : blockIdx.x;
-  const int bh = logical / nqt;
-  int qt = logical % nqt;
+  int bh, qt;
+  head_tile(logical, nqt, (int)(total / nqt), bh, qt);
   if (CAUSAL) qt = nqt - 1 - qt;
   const int q0 = qt * kBR;
   const int qw = q0 + qblk * 32;

@@ -64,15 +64,16 @@ struct DecodeArgs {
 };
 
 // Whether a grid of `total` work items over `heads` heads uses the XCD-aware order (xcd_remap in
-// fa_common.h: consecutive work items, i.e. the tiles of one head, on one XCD so that they share its
-// L2).  That order hands each XCD a contiguous eighth of the items.  Without the causal mask every tile
-// costs the same, so any contiguous eighth is a fair share.  Under the mask a head's tiles range from
-// one key tile to all of them.  With fewer heads than XCDs, the eighths split single heads, and the
-// XCD holding a head's heaviest tiles gets up to twice its share.  Measured at d = 128: one head of
-// 2^20 keys ran 1.7x faster in the plain order (dealt to the XCDs round-robin, which mixes heavy and
-// light tiles on every XCD), two heads 1.5x and six heads 1.06-1.15x.  From eight heads on each XCD
-// holds at least one whole head's worth: twelve heads ran 8-14% faster in the XCD order (L2 reuse
-// outweighs the residual imbalance), 128 heads the same either way.
+// fa_common.h: consecutive work items, i.e. the tiles of one group of heads (head_tile), on one XCD
+// so that they share its L2).  That order hands each XCD a contiguous eighth of the items.  Without
+// the causal mask every tile costs the same, so any contiguous eighth is a fair share.  Under the
+// mask a head's tiles range from one key tile to all of them.  With fewer heads than XCDs, the
+// eighths split single heads, and the XCD holding a head's heaviest tiles gets up to twice its
+// share.  Measured at d = 128 (heads taken one at a time): one head of 2^20 keys ran 1.7x faster in
+// the plain order (dealt to the XCDs round-robin, which mixes heavy and light tiles on every XCD),
+// two heads 1.5x and six heads 1.06-1.15x.  From eight heads on each XCD holds at least one whole
+// head's worth: twelve heads ran 8-14% faster in the XCD order (L2 reuse outweighs the residual
+// imbalance), 128 heads the same either way.
 inline int use_xcd_order(uint32_t total, long heads, int causal) {
   return (total % 8u == 0u && (!causal || heads >= 8)) ? 1 : 0;
 }
