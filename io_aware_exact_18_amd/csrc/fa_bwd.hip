@@ -132,7 +132,7 @@ __global__ __launch_bounds__(kThreads, (D == 256 && OUT != 1) ? 1 : 2) void bwd_
     logical %= per_seg;
   }
   int bh, kt;  // key blocks in order, heaviest first under the causal mask
-  head_tile(logical, nkt, SPLIT ? so.bh_count : (int)(gridDim.x / nkt), bh, kt);
+  head_tile(logical, nkt, SPLIT ? so.bh_count : (int)(gridDim.x / nkt), remap, bh, kt);
   const int k0 = kt * kBKV;
   const int kw = k0 + 32 * wave;  // first key of this wave
   const int kj = kw + lc;         // this lane's key (column of the score tiles)
@@ -361,7 +361,7 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void bwd_dq_kernel(
     logical %= per_seg;
   }
   int bh, qt;
-  head_tile(logical, nqt, SPLIT ? so.bh_count : (int)(gridDim.x / nqt), bh, qt);
+  head_tile(logical, nqt, SPLIT ? so.bh_count : (int)(gridDim.x / nqt), remap, bh, qt);
   if (CAUSAL) qt = nqt - 1 - qt;  // heaviest tiles first
   const int q0 = qt * kBR;
   const int qw = q0 + 32 * wave;

@@ -316,22 +316,27 @@ __device__ inline uint32_t xcd_remap(uint32_t bid, uint32_t total) {
 }
 
 // Logical work item → (head, tile) for grids of `ntile` tiles per head, tiles numbered in the order
-// they should start (under the causal mask: heaviest first).  Heads are taken in groups of
-// kHeadGroup, and within a group the items alternate between the heads tile by tile: item
-// G·T·p + G·t + i is tile t of head G·p + i (the last group may hold fewer heads).  Causal tiles
-// range from one key tile to all of them, and workgroups start in item order as slots free up.
-// Head by head, the last heads of a dispatch queue start their heaviest tiles late and leave compute
-// units idle at the end; in groups, every group's heaviest tiles start together, and the workgroups in
-// flight still cover few heads, whose K and V (or Q and dO) they share through L2.  Measured on
-// MI355X, causal 4 × 32 × 4096 × 128 (one process, bit-identical results), head by head → groups of
-// 4: forward 0.625 → 0.569 ms, dK/dV 1.154 → 1.045, dQ 0.814 → 0.759; groups of 8 were 1% slower than
-// groups of 4, and a uniform (non-causal) grid is unchanged.
+// they should start (under the causal mask: heaviest first).  Heads are taken in groups of G, and
+// within a group the items alternate between the heads tile by tile: item G·T·p + G·t + i is tile t of
+// head G·p + i (the last group may hold fewer heads).  Causal tiles range from one key tile to all of
+// them, and workgroups start in item order as slots free up.  Head by head, the last heads of a
+// dispatch queue start their heaviest tiles late and leave compute units idle at the end; in groups,
+// every group's heaviest tiles start together, and the workgroups in flight still cover few heads,
+// whose K and V (or Q and dO) they share through L2.  G is kHeadGroup, except in the XCD order
+// (`remap`: each XCD takes a contiguous eighth of the items), where a group must not span XCDs — the
+// first XCD would take the heaviest tiles of several heads and the last their lightest — so G is at
+// most the heads per XCD.  Measured on MI355X, causal 4 × 32 × 4096 × 128 (one process,
+// bit-identical results), head by head → groups of 4: forward 0.625 → 0.569 ms, dK/dV 1.154 →
+// 1.045, dQ 0.814 → 0.759; groups of 8 were 1% slower than groups of 4, and a uniform (non-causal)
+// grid is unchanged.
 constexpr int kHeadGroup = 4;
-__device__ inline void head_tile(uint32_t item, int ntile, int nheads, int& head, int& tile) {
-  const int span = kHeadGroup * ntile;
+__device__ inline void head_tile(uint32_t item, int ntile, int nheads, int remap, int& head,
+                                 int& tile) {
+  const int G = remap ? max(1, min(kHeadGroup, nheads / 8)) : kHeadGroup;
+  const int span = G * ntile;
   const int grp = (int)item / span;
-  const int base = grp * kHeadGroup;
-  const int gn = min(kHeadGroup, nheads - base);  // heads in this group
+  const int base = grp * G;
+  const int gn = min(G, nheads - base);  // heads in this group
   const int idx = (int)item - grp * span;
   tile = idx / gn;
   head = base + idx % gn;
