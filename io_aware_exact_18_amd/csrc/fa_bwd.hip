@@ -44,6 +44,11 @@ constexpr int kBKV = 128;  // dK/dV kernel: keys per workgroup (32 per wave)
 constexpr int kBQ = 32;    // dK/dV kernel: queries per step
 constexpr int kBR = 128;   // dQ kernel: queries per workgroup (32 per wave)
 constexpr int kBC = 64;    // dQ kernel: keys per tile
+// Resident workgroups per compute unit (registers and LDS), for the grid order (head_tile).
+template <int D>
+constexpr int dq_per_cu() { return D == 64 ? 3 : D == 256 ? 1 : 2; }
+template <int D, int OUT>
+constexpr int dkdv_per_cu() { return D == 64 ? 3 : (D == 256 && OUT == 2) ? 1 : 2; }
 
 // ---------------------------------------------------------------------------------------------------
 // 1. D_i = Σ_t dO_it O_it, stored negated.  One row per pre_tpr<D>() threads (a power of two), each
@@ -132,7 +137,8 @@ __global__ __launch_bounds__(kThreads, (D == 256 && OUT != 1) ? 1 : 2) void bwd_
     logical %= per_seg;
   }
   int bh, kt;  // key blocks in order, heaviest first under the causal mask
-  head_tile(logical, nkt, SPLIT ? so.bh_count : (int)(gridDim.x / nkt), remap, bh, kt);
+  head_tile(logical, nkt, SPLIT ? so.bh_count : (int)(gridDim.x / nkt), remap,
+            dkdv_per_cu<D, OUT>(), bh, kt);
   const int k0 = kt * kBKV;
   const int kw = k0 + 32 * wave;  // first key of this wave
   const int kj = kw + lc;         // this lane's key (column of the score tiles)
@@ -361,7 +367,8 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void bwd_dq_kernel(
     logical %= per_seg;
   }
   int bh, qt;
-  head_tile(logical, nqt, SPLIT ? so.bh_count : (int)(gridDim.x / nqt), remap, bh, qt);
+  head_tile(logical, nqt, SPLIT ? so.bh_count : (int)(gridDim.x / nqt), remap, dq_per_cu<D>(),
+            bh, qt);
   if (CAUSAL) qt = nqt - 1 - qt;  // heaviest tiles first
   const int q0 = qt * kBR;
   const int qw = q0 + 32 * wave;

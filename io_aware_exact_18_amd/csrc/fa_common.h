@@ -317,22 +317,26 @@ __device__ inline uint32_t xcd_remap(uint32_t bid, uint32_t total) {
 
 // Logical work item → (head, tile) for grids of `ntile` tiles per head, tiles numbered in the order
 // they should start (under the causal mask: heaviest first).  Heads are taken in groups of G, and
-// within a group the items alternate between the heads tile by tile: item G·T·p + G·t + i is tile t of
-// head G·p + i (the last group may hold fewer heads).  Causal tiles range from one key tile to all of
-// them, and workgroups start in item order as slots free up.  Head by head, the last heads of a
-// dispatch queue start their heaviest tiles late and leave compute units idle at the end; in groups,
-// every group's heaviest tiles start together, and the workgroups in flight still cover few heads,
-// whose K and V (or Q and dO) they share through L2.  G is kHeadGroup, except in the XCD order
-// (`remap`: each XCD takes a contiguous eighth of the items), where a group must not span XCDs — the
-// first XCD would take the heaviest tiles of several heads and the last their lightest — so G is at
-// most the heads per XCD.  Measured on MI355X, causal 4 × 32 × 4096 × 128 (one process,
-// bit-identical results), head by head → groups of 4: forward 0.625 → 0.569 ms, dK/dV 1.154 →
-// 1.045, dQ 0.814 → 0.759; groups of 8 were 1% slower than groups of 4, and a uniform (non-causal)
-// grid is unchanged.
+// within a group the items alternate between the heads tile by tile: item G·T·p + G·t + i is tile t
+// of head G·p + i (the last group may hold fewer heads).  Causal tiles range from one key tile to
+// all of them, and workgroups start in item order as slots free up.  Head by head, the last heads
+// of a dispatch queue start their heaviest tiles late and leave compute units idle at the end; in
+// groups, every group's heaviest tiles start together, and the workgroups in flight still cover few
+// heads, whose K and V (or Q and dO) they share through L2.  G is kHeadGroup when a head has fewer
+// tiles than an XCD runs workgroups at once (32 compute units × `per_cu` resident workgroups); with
+// more, the queue is long enough for heads one at a time to finish evenly (measured: the forward of
+// 32 heads of 16384 keys took the same time either way, and reads 2.8× instead of 1.3× its
+// algorithmic bytes from beyond L2 in groups), so G is 1.  In the XCD order (`remap`: each XCD
+// takes a contiguous eighth of the items) a group must not span XCDs — the first XCD would take the
+// heaviest tiles of several heads and the last their lightest — so G is at most the heads per XCD.
+// Measured on MI355X, causal 4 × 32 × 4096 × 128 (one process, bit-identical results), head by head
+// → groups of 4: forward 0.625 → 0.569 ms, dK/dV 1.154 → 1.045, dQ 0.814 → 0.759; groups of 8 were
+// 1% slower than groups of 4, and a uniform (non-causal) grid is unchanged.
 constexpr int kHeadGroup = 4;
-__device__ inline void head_tile(uint32_t item, int ntile, int nheads, int remap, int& head,
-                                 int& tile) {
-  const int G = remap ? max(1, min(kHeadGroup, nheads / 8)) : kHeadGroup;
+__device__ inline void head_tile(uint32_t item, int ntile, int nheads, int remap, int per_cu,
+                                 int& head, int& tile) {
+  int G = ntile < 32 * per_cu ? kHeadGroup : 1;
+  if (remap) G = max(1, min(G, nheads / 8));
   const int span = G * ntile;
   const int grp = (int)item / span;
   const int base = grp * G;

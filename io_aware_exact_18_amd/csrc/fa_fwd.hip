@@ -116,7 +116,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     logical %= per_seg;
   }
   int bh, qt;  // tile order: heaviest first under the causal mask
-  head_tile(logical, nqt, SPLIT ? so.bh_count : (int)(total / nqt), remap, bh, qt);
+  head_tile(logical, nqt, SPLIT ? so.bh_count : (int)(total / nqt), remap, D == 64 ? 3 : 2, bh,
+            qt);
   if (CAUSAL) qt = nqt - 1 - qt;
   const int q0 = qt * kBR;
   const int qw = q0 + wave * 32;  // first query of this wave
@@ -361,7 +362,7 @@ __global__ __launch_bounds__(kSplitThreads, 1) void fwd_bf16_split_kernel(
   const uint32_t total = gridDim.x;
   const uint32_t logical = remap ? xcd_remap(blockIdx.x, total) : blockIdx.x;
   int bh, qt;
-  head_tile(logical, nqt, (int)(total / nqt), remap, bh, qt);
+  head_tile(logical, nqt, (int)(total / nqt), remap, 1, bh, qt);
   if (CAUSAL) qt = nqt - 1 - qt;
   const int q0 = qt * kBR;
   const int qw = q0 + qblk * 32;

@@ -118,7 +118,7 @@ __global__ __launch_bounds__(kThreads, D <= 128 ? 3 : 2) void fwd_fp8_kernel(
   const uint32_t item = col_splits<D>() == 2 ? logical >> 1 : logical;
   int bh, qt;
   head_tile(item, nqt, SPLIT ? so.bh_count : (int)(gridDim.x / col_splits<D>() / nqt), remap,
-            bh, qt);
+            D <= 128 ? 3 : 2, bh, qt);
   if (CAUSAL) qt = nqt - 1 - qt;
   const int q0 = qt * kBR;
   const int qw = q0 + 32 * wave;
