@@ -316,34 +316,47 @@ __device__ inline uint32_t xcd_remap(uint32_t bid, uint32_t total) {
 }
 
 // Logical work item → (head, tile) for grids of `ntile` tiles per head, tiles numbered in the order
-// they should start (under the causal mask: heaviest first).  Heads are taken in groups of G, and
-// within a group the items alternate between the heads tile by tile: item G·T·p + G·t + i is tile t
-// of head G·p + i (the last group may hold fewer heads).  Causal tiles range from one key tile to
-// all of them, and workgroups start in item order as slots free up.  Head by head, the last heads
-// of a dispatch queue start their heaviest tiles late and leave compute units idle at the end; in
+// they should start (under the causal mask: heaviest first). Heads are taken in groups, and within
+// a group the items alternate between the heads tile by tile: the items of a group of g heads
+// starting at head h are g·t + i → tile t of head h + i. Causal tiles range from one key tile to
+// all of them, and workgroups start in item order as slots free up. Head by head, the last heads of
+// a dispatch queue start their heaviest tiles late and leave compute units idle at the end; in
 // groups, every group's heaviest tiles start together, and the workgroups in flight still cover few
-// heads, whose K and V (or Q and dO) they share through L2.  G is kHeadGroup when a head has fewer
-// tiles than an XCD runs workgroups at once (32 compute units × `per_cu` resident workgroups); with
-// more, the queue is long enough for heads one at a time to finish evenly (measured: the forward of
-// 32 heads of 16384 keys took the same time either way, and reads 2.8× instead of 1.3× its
-// algorithmic bytes from beyond L2 in groups), so G is 1.  In the XCD order (`remap`: each XCD
-// takes a contiguous eighth of the items) a group must not span XCDs — the first XCD would take the
-// heaviest tiles of several heads and the last their lightest — so G is at most the heads per XCD.
-// Measured on MI355X, causal 4 × 32 × 4096 × 128 (one process, bit-identical results), head by head
-// → groups of 4: forward 0.625 → 0.569 ms, dK/dV 1.154 → 1.045, dQ 0.814 → 0.759; groups of 8 were
-// 1% slower than groups of 4, and a uniform (non-causal) grid is unchanged.
+// heads, whose K and V (or Q and dO) they share through L2. Groups hold kHeadGroup heads, the last
+// one also the remainder (a short last group would end the queue on its heaviest tiles again). In
+// the XCD order (`remap`: each XCD takes a contiguous eighth of the items) the heads are grouped
+// within each XCD's eighth, so that no group spans two XCDs (the first would take the heaviest
+// tiles of several heads, the other their lightest); when the head count is not a multiple of 8 the
+// eighths cut heads anyway, and the heads are taken one at a time. They are also taken one at a
+// time when a head has at least as many tiles as an XCD holds workgroups at once (32 compute units
+// × `per_cu` resident workgroups): the queue then finishes evenly, and groups would only cost L2
+// reuse (the forward of 32 heads of 16384 keys took the same time either way, and read 2.8× instead
+// of 1.3× its algorithmic bytes from beyond L2 in groups). Measured on MI355X, causal 4 × 32 × 4096
+// × 128 (one process, bit-identical results), one head at a time → groups of 4: forward 0.625 →
+// 0.569 ms, dK/dV 1.154 → 1.045, dQ 0.814 → 0.759; groups of 3 or 6 (leaving a short last group per
+// XCD) were 3–8% slower than groups of 4, groups of 8 1%.
 constexpr int kHeadGroup = 4;
 __device__ inline void head_tile(uint32_t item, int ntile, int nheads, int remap, int per_cu,
                                  int& head, int& tile) {
-  int G = ntile < 32 * per_cu ? kHeadGroup : 1;
-  if (remap) G = max(1, min(G, nheads / 8));
-  const int span = G * ntile;
-  const int grp = (int)item / span;
-  const int base = grp * G;
-  const int gn = min(G, nheads - base);  // heads in this group
-  const int idx = (int)item - grp * span;
+  if (ntile >= 32 * per_cu || (remap && nheads % 8 != 0)) {  // one head at a time
+    head = (int)item / ntile;
+    tile = (int)item % ntile;
+    return;
+  }
+  int h0 = 0, nh = nheads, it = (int)item;
+  if (remap) {  // group within each XCD's eighth of the heads
+    nh = nheads / 8;
+    const int x = it / (nh * ntile);
+    h0 = x * nh;
+    it -= x * nh * ntile;
+  }
+  const int ng = max(1, nh / kHeadGroup);  // groups; the last takes the remainder
+  const int span = kHeadGroup * ntile;
+  const int grp = min(it / span, ng - 1);
+  const int gn = grp == ng - 1 ? nh - grp * kHeadGroup : kHeadGroup;  // heads in this group
+  const int idx = it - grp * span;
   tile = idx / gn;
-  head = base + idx % gn;
+  head = h0 + grp * kHeadGroup + idx % gn;
 }
 
 }  // namespace fa
