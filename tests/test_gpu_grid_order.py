@@ -1,9 +1,10 @@
 """GPU parity across the grid orders of the tiled kernels, against the fp64 CPU oracle.
 
 The forward, dQ and dK/dV kernels map their work items to (head, tile) in groups of heads whose
-tiles alternate (head_tile in the library's shared header).  The group size depends on the head
-count, the tiles per head and, under the causal mask with at least eight heads, the XCD order, where
-a group holds at most ⌊heads / 8⌋ heads (1, 2, 3 or 4 here).  Every mapping must cover each
+tiles alternate (head_tile in the library's shared header): groups of four, the last one taking the
+remainder, formed within each XCD's eighth of the heads in the XCD order (causal grids with at
+least eight heads), or heads one at a time (head count not a multiple of 8 in that order, or many
+tiles per head).  Every mapping must cover each
 (head, tile) exactly once; a wrong one leaves rows unwritten or writes a head's rows twice.  Two
 checks see that on every row of every head: each head's outputs are bit for bit those of the same
 head computed alone (a one-head grid, whose order is trivial; a tile's arithmetic does not depend on
@@ -51,9 +52,12 @@ def _rel_fro(got, ref):
     return np.linalg.norm(got - ref) / (den if den > 0 else 1.0)
 
 
-# (B, H, N, d, causal): head counts 8..40 put the causal grids in the XCD order with groups of 1, 2,
-# 3 and 4 heads (⌊BH/8⌋ capped at 4); 5 and 13 heads leave a partial last group in the plain order.
+# (B, H, N, d, causal): causal grids of 8, 16, 24, 40 and 56 heads take the XCD order with 1, 2, 3,
+# 5 and 7 heads per XCD (one group, or a group of four and one taking the remainder); 12 heads take
+# it one head at a time; 5 and 13 heads take the plain order with a last group taking the remainder.
 CASES = [
+    (1, 56, 128, 64, True),
+    (1, 12, 256, 128, True),
     (1, 8, 640, 128, True),
     (2, 8, 384, 64, True),
     (4, 6, 300, 128, True),
