@@ -311,7 +311,7 @@ __device__ inline void merge_partials(const float* __restrict__ part_o,
 
 // blockIdx → logical work item such that consecutive logical items land on the same XCD: logical
 // item L runs on XCD L / (total / 8).  Used only when total is a multiple of 8.
-__device__ inline uint32_t xcd_remap(uint32_t bid, uint32_t total) {
+__host__ __device__ inline uint32_t xcd_remap(uint32_t bid, uint32_t total) {
   return (bid % 8u) * (total / 8u) + bid / 8u;
 }
 
@@ -336,8 +336,8 @@ __device__ inline uint32_t xcd_remap(uint32_t bid, uint32_t total) {
 // 0.569 ms, dK/dV 1.154 → 1.045, dQ 0.814 → 0.759; groups of 3 or 6 (leaving a short last group per
 // XCD) were 3–8% slower than groups of 4, groups of 8 1%.
 constexpr int kHeadGroup = 4;
-__device__ inline void head_tile(uint32_t item, int ntile, int nheads, int remap, int per_cu,
-                                 int& head, int& tile) {
+__host__ __device__ inline void head_tile(uint32_t item, int ntile, int nheads, int remap,
+                                          int per_cu, int& head, int& tile) {
   if (ntile >= 32 * per_cu || (remap && nheads % 8 != 0)) {  // one head at a time
     head = (int)item / ntile;
     tile = (int)item % ntile;
