@@ -219,6 +219,28 @@ def traffic_sweep(fa, torch, steps):
         del q, k, v, o, lse
 
 
+# The secondary legs each start after idle host work (building their inputs). After such a pause the
+# shader clock starts low and climbs over the first tens of milliseconds of load (kernel traces of
+# causal_4k: steps of 3.0 ms falling to 2.24 ms over the first ~20). A secondary leg therefore warms
+# up for at least `warmup` calls and at least SETTLE_S seconds of load before its timed calls, so
+# that it is timed at the settled clock. The headline leg runs exactly the warm-up steps it is given.
+SETTLE_S = 0.25
+
+
+def settle(run, warmup, min_s=SETTLE_S):
+    """Call run() at least `warmup` times and until min_s seconds of wall time have passed,
+    synchronising every fourth call so that wall time follows the device's work."""
+    import torch
+    t0 = time.perf_counter()
+    n = 0
+    while n < warmup or time.perf_counter() - t0 < min_s:
+        run()
+        n += 1
+        if n % 4 == 0:
+            torch.cuda.synchronize()
+    return n
+
+
 def decode_measure(fa, workloads, lib, steps, warmup):
     """Secondary measurement: decoding against a key/value cache (both decoding workloads), timed
     with events around fa_decode (split and merge kernels).  HBM-bound: priced against 8 TB/s with
@@ -249,8 +271,7 @@ def decode_measure(fa, workloads, lib, steps, warmup):
             if code != 0:
                 raise fa.FaError("fa_decode", code, fa.status_str(code))
 
-        for _ in range(warmup):
-            run()
+        settle(run, warmup)
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
         ev[0].record(stream)
         for _ in range(steps):
@@ -290,8 +311,7 @@ def fp8_forward(fa, workloads, lib, steps, warmup, name="fp8_8k"):
         if code != 0:
             raise fa.FaError("fa_fwd_fp8", code, fa.status_str(code))
 
-    for _ in range(warmup):
-        run()
+    settle(run, warmup)
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
     ev[0].record(stream)
     for _ in range(steps):
@@ -339,9 +359,7 @@ def fp8_backward(fa, workloads, lib, steps, warmup):
         if code != 0:
             raise fa.FaError("fa_bwd_fp8", code, fa.status_str(code))
 
-    for _ in range(warmup):
-        fwd()
-        bwd()
+    settle(lambda: (fwd(), bwd()), warmup)
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
     for e in ev:
         e[0].record(stream)
@@ -406,8 +424,7 @@ def fwd_bwd_secondary(fa, workloads, lib, name, steps, warmup):
         ev[3].record(stream)
 
     spare = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
-    for _ in range(warmup):
-        step(spare)
+    settle(lambda: step(spare), warmup)
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
     for i in range(steps):
         step(events[i])
@@ -473,8 +490,7 @@ def split_secondary(fa, workloads, lib, name, steps, warmup):
            "fwd_split_workspace_bytes": ws_f, "bwd_split_workspace_bytes": ws_b}
     for label, fn in (("unsplit", plain), ("split", split)):
         spare = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
-        for _ in range(warmup):
-            fn(spare)
+        settle(lambda: fn(spare), warmup)
         events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
         for i in range(steps):
             fn(events[i])

@@ -43,3 +43,19 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_settle_runs_at_least_the_warmup_and_the_settling_time(monkeypatch):
+    """The secondary legs' warm-up: at least `warmup` calls, and calls until the settling time has
+    passed; device synchronisation replaced by a no-op (no GPU here)."""
+    import time
+    import torch
+    syncs = []
+    monkeypatch.setattr(torch.cuda, "synchronize", lambda *a: syncs.append(1))
+    calls = []
+    assert bench.settle(lambda: calls.append(1), 7, min_s=0.0) == 7 == len(calls)
+    calls.clear()
+    t0 = time.perf_counter()
+    n = bench.settle(lambda: (calls.append(1), time.sleep(0.002)), 1, min_s=0.05)
+    assert time.perf_counter() - t0 >= 0.05 and n == len(calls) > 1
+    assert len(syncs) >= n // 4 > 0
