@@ -36,6 +36,10 @@
 //     with the Q operand in registers and the next tile's scores overlapping the exponentials
 //     (bit-identical outputs), causal 4 × 32 × 8192: d = 128 1.345 → 1.274 ms, d = 96 1.212 →
 //     1.148 ms, d = 64 within 1%.  d = 256 keeps its Q operand in registers at two waves per SIMD.
+//     The causal kernels, whose row sum takes 12 fewer registers (below), hold it in registers too,
+//     still at three waves per SIMD (four at d = 64: 120 registers); bit-identical, 4 × 32 × 8192:
+//     d = 64 0.744 → 0.733 ms, d = 128 1.144 → 1.119, d = 96 unchanged.  The non-causal kernels
+//     need the room.
 //   * Head dims: Sᵀ takes D/64 k-steps of 64, Oᵀ D/32 column blocks of 32.  d = 96 uses the d = 128
 //     LDS rows: the DMA fills bytes 96..127 of each K and V row with zeros and the Q operand's last
 //     32 columns are zero, so the second k-step adds nothing, and only three V column blocks are read.
@@ -107,9 +111,10 @@ __global__ __launch_bounds__(kThreads, D <= 128 ? 3 : 2) void fwd_fp8_kernel(
   __shared__ __attribute__((aligned(1024))) uint8_t k1s[kBC * LR];
   __shared__ __attribute__((aligned(1024))) uint8_t v0s[kBC * LR];
   __shared__ __attribute__((aligned(1024))) uint8_t v1s[kBC * LR];
-  // The workgroup's Q rows (d ≤ 128): B-operand fragments are read from here each tile instead of
-  // being held in registers, which keeps the kernel within three waves per SIMD.
-  constexpr bool QLDS = D <= 128;
+  // The workgroup's Q rows (non-causal, d ≤ 128): B-operand fragments are read from here each tile
+  // instead of being held in registers, which keeps the kernel within three waves per SIMD (four at
+  // d = 64).
+  constexpr bool QLDS = D <= 128 && !CAUSAL;
   __shared__ __attribute__((aligned(1024))) uint8_t qs[QLDS ? kBR * LR : 16];
 
   const int tid = threadIdx.x;
@@ -149,14 +154,18 @@ __global__ __launch_bounds__(kThreads, D <= 128 ? 3 : 2) void fwd_fp8_kernel(
   const auto mv = make_rsrc(V + head, head_bytes);
   const TileCopy<LR, kBC, kThreads, D> copy(tid, [](int r) { return swz8<LR>(r); });
 
-  // Qᵀ operand (B) in registers (d = 256): this lane's query, k-step s covers d = 64s + 32g .. +31.
-  // At d ≤ 128 the same fragments are read from the Q rows in LDS, whose columns past D (d = 96) the
-  // copy fills with zeros.
+  // Qᵀ operand (B) in registers (causal, and d = 256): this lane's query, k-step s covers
+  // d = 64s + 32g .. +31.  Columns past D (d = 96: s = 1, g = 1) are read from an offset past the
+  // buffer's range (per-head bytes stay below 2^31), which returns zeros.  Otherwise the same
+  // fragments are read from the Q rows in LDS, whose columns past D the copy fills with zeros.
   i32x8 qf[QLDS ? 1 : KS];
   if constexpr (!QLDS) {
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
       uint32_t off = (uint32_t)(qi * D + 64 * s + 32 * g);
+      if constexpr (D == 96) {
+        if (s == 1 && g == 1) off = 0x80000000u;
+      }
       const u32x4 lo = buf_load16(rq, off), hi = buf_load16(rq, off + 16);
       qf[s] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
                     (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
