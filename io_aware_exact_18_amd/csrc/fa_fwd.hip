@@ -30,8 +30,8 @@
 //     rounded to bf16 — the weights the P·V product actually applies — which O is divided by.  O is
 //     then an exactly normalised average of V rows under the rounded weights: in a row dominated by
 //     one key it returns that key's V row however p rounds, where dividing by l would leave p's
-//     rounding error (up to 2^-9 of |V|) in O.  Causal instantiations form lr on the matrix core
-//     (a 16×16×32 product against a selector operand, in the kernel below).
+//     rounding error (up to 2^-9 of |V|) in O.  lr is formed on the matrix core (a 16×16×32
+//     product against a selector operand, in the kernel below).
 //   * Grid: one workgroup per (batch·head, query tile); the query tiles of a group of four heads are
 //     kept on one XCD so the heads' K/V stay in that XCD's L2, interleaved head by head so that under
 //     the causal mask every group's heaviest tiles start first (head_tile in fa_common.h).
@@ -145,7 +145,12 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     qf[s] = __builtin_bit_cast(bf16x8, buf_load16(rq, (uint32_t)(qi * D + 16 * s + 8 * g) * 2u));
 
   // Tiles at or beyond this index are fully masked for this wave (causal): no math on them.
-  const int wave_tiles = CAUSAL ? min(t_end, (qw + 31) / kBC + 1) : t_end;
+  int wave_tiles = CAUSAL ? min(t_end, (qw + 31) / kBC + 1) : t_end;
+  // Without the mask every wave takes every tile, and the compiler would drop the `j < wave_tiles`
+  // test below and schedule the two unrolled tiles as one block: that needed 177 registers at
+  // d = 64 (a wave per SIMD fewer) and spilled at d = 128.  An opaque count keeps the test, and the
+  // non-causal instantiations compile to the causal ones' register counts.
+  if constexpr (!CAUSAL) asm volatile("" : "+s"(wave_tiles));
   const FragOffsets<L> fo(lane);
 
   // Prologue: K(t_beg), K(t_beg + 1), V(t_beg) in flight; scores of tile t_beg.
@@ -172,19 +177,16 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
 
   float m = -INFINITY;  // reference maximum of the base-2 scaled scores (see kSlack)
   float l = 0.f;        // running sum of 2^(t - m) over this lane's keys (half of the row)
-  float lr = 0.f;       // the same sum over the bf16-rounded values that enter P·V
-  // Causal instantiations take lr on the matrix core instead: a 16×16×32 product of the Pᵀ operand
-  // against a selector operand (the FP8 forward's row-sum scheme: A-operand lane l is row l % 16 of
-  // k-group l / 16, Pᵀ lane l is column l % 16 of k-group l / 16 and holds query l % 32; rows 0 and
-  // 8 select k-groups 0 and 2, rows 4 and 12 groups 1 and 3), so register 0 of every lane holds its
-  // query's sum over both key halves.  Four products per tile replace 16 dot2 instructions and the
-  // final exchange between the half-waves.  Measured on MI355X, causal 4 × 32 × 4096 (O within one
-  // bf16 ulp, LSE bit-identical): d = 128 0.558 → 0.538 ms, d = 96 0.469 → 0.452, d = 64 (8 × 16 ×
-  // 2048) 0.116 → 0.111.  The non-causal instantiations keep the dot2 sum: with the selector's
-  // lane-dependent registers, which the compiler cannot rematerialise, d = 64 needed 177 registers
-  // (a wave per SIMD fewer) and d = 128 spilled.
-  constexpr bool LR16 = CAUSAL;
-  f32x4 lacc = {0.f, 0.f, 0.f, 0.f};
+  // lr, the same sum over the bf16-rounded values that enter P·V, is taken on the matrix core: a
+  // 16×16×32 product of the Pᵀ operand against a selector operand (the FP8 forward's row-sum scheme:
+  // A-operand lane l is row l % 16 of k-group l / 16, Pᵀ lane l is column l % 16 of k-group l / 16
+  // and holds query l % 32; rows 0 and 8 select k-groups 0 and 2, rows 4 and 12 groups 1 and 3), so
+  // register 0 of every lane holds its query's sum over both key halves.  Four products per tile replace 16 dot2 instructions and the final exchange
+  // between the half-waves.  Measured on MI355X in one process (O within one bf16 ulp, LSE
+  // bit-identical), causal 4 × 32 × 4096: d = 128 0.558 → 0.538 ms, d = 96 0.469 → 0.452, d = 64
+  // (8 × 16 × 2048) 0.116 → 0.111; non-causal: d = 128 1.085 → 1.043, d = 96 0.889 → 0.864, d = 64
+  // (8 × 16 × 2048) 0.191 → 0.182.
+  f32x4 lacc = {0.f, 0.f, 0.f, 0.f};  // lr: register 0
   const __bf16 one = ((lane & 3) == 0 && ((lane >> 2) & 1) == ((lane >> 4) & 1)) ? (__bf16)1.0f
                                                                                    : (__bf16)0.0f;
   const bf16x8 sel = {one, one, one, one, one, one, one, one};
@@ -227,12 +229,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
         const float m_new = fmaxf(m, mt);
         const float alpha = exp2_fast(m - (m_new == -INFINITY ? 0.f : m_new));
         l *= alpha;
-        if constexpr (LR16) {
 #pragma unroll
-          for (int r = 0; r < 4; ++r) lacc[r] *= alpha;
-        } else {
-          lr *= alpha;
-        }
+        for (int r = 0; r < 4; ++r) lacc[r] *= alpha;
 #pragma unroll
         for (int b = 0; b < DB; ++b)
 #pragma unroll
@@ -284,10 +282,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
         for (int r = (kb == 0 ? 4 : 0); r < 16; ++r) rs[r & 3] += s_cur[kb][r];
       l += (rs[0] + rs[1]) + (rs[2] + rs[3]);
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        if constexpr (LR16) lacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sel, pf[ks], lacc, 0, 0, 0);
-        else lr = sum_bf16x8(pf[ks], lr);
-      }
+      for (int ks = 0; ks < 4; ++ks)
+        lacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sel, pf[ks], lacc, 0, 0, 0);
       mx = rowmax(s_nxt);
 #pragma unroll
       for (int i = 0; i < 2 * KSTEPS; ++i) {
@@ -308,7 +304,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     // The segment's partial result: unnormalised Oᵀ column, reference maximum and both row sums (a
     // wave without keys in the segment writes m = −inf and zeros, which the merge weighs by 0).
     const float l_seg = halves_sum(l);
-    const float lr_seg = LR16 ? lacc[0] : halves_sum(lr);
+    const float lr_seg = lacc[0];
     if (qi < N) {
       const size_t row = ((size_t)sg * so.bh_count + bh) * N + qi;
       float* orow = so.part_o + row * D;
@@ -331,7 +327,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
 
   // Epilogue: combine the two half-row sums, normalise by the rounded weights' sum, write O and LSE.
   const float l_tot = halves_sum(l);
-  const float inv = 1.f / (LR16 ? lacc[0] : halves_sum(lr));
+  const float inv = 1.f / lacc[0];
   if (qi < N) {
     bf16* orow = O + head + (size_t)qi * D;
 #pragma unroll

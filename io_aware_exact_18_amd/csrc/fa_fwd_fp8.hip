@@ -15,31 +15,29 @@
 //     the FMA's constant) keeps small probabilities out of e4m3's subnormal range; both cancel in
 //     O = Σ P V / Σ P and are removed from LSE.  The row sum l is formed by one more
 //     matrix-core op on the Pᵀ operand, so it sums exactly the rounded P values that enter P·V (a
-//     tile's sum of e4m3 values between 2^-9 and 2^8 is exact in fp32, in any order).  Causal
-//     instantiations use v_mfma_f32_16x16x128_f8f6f4 against a selector operand (below): half the
-//     cycles of a 32×32×64 product and 4 accumulator registers instead of 16.  Measured on MI355X,
-//     causal 4 × 32 × 8192 (bit-identical outputs): d = 64 0.845 → 0.801 ms, d = 96 1.115 → 1.065,
-//     d = 128 1.239 → 1.201.  Non-causal instantiations keep the 32×32×64 product against an
-//     all-ones operand: they sit at the register limit, and the selector's lane-dependent registers
-//     (which the compiler cannot rematerialise, unlike a constant) push them into spills (d = 128
-//     ran 3× slower, d = 64 lost its fourth wave per SIMD).
+//     tile's sum of e4m3 values between 2^-9 and 2^8 is exact in fp32, in any order): a
+//     v_mfma_f32_16x16x128_f8f6f4 against a selector operand (below), half the cycles of a
+//     32×32×64 product against all ones and 4 accumulator registers instead of 16.  Measured on
+//     MI355X against that form (bit-identical outputs), causal 4 × 32 × 8192: d = 64 0.845 →
+//     0.801 ms, d = 96 1.115 → 1.065, d = 128 1.239 → 1.201.
 //   * Key order: each wave loads K rows into the A operand with bits 2 and 3 of the row index swapped,
 //     so that every lane's 32 probabilities form four runs of 8 consecutive keys; V is then read with
 //     ds_read_b64_tr_b8, which hands each lane 8 consecutive key rows of one column, and the P bytes
 //     go straight from the score accumulator into the B operand.
 //   * Tiles: 4 waves × 32 queries per workgroup, 64-key K/V tiles copied into LDS by buffer→LDS DMA,
 //     K one tile ahead of V, double-buffered, rows XOR-swizzled for conflict-free reads.
-//   * Three waves per SIMD at d ≤ 128 (at most 168 registers, 48 KiB of LDS per workgroup): the Q
-//     operand is read from the workgroup's Q rows in LDS each tile instead of being held in
-//     registers, and one score tile is live at a time (the next tile's scores are formed after the
-//     exponentials of the current one have read it).  Measured on MI355X against two waves per SIMD
-//     with the Q operand in registers and the next tile's scores overlapping the exponentials
-//     (bit-identical outputs), causal 4 × 32 × 8192: d = 128 1.345 → 1.274 ms, d = 96 1.212 →
-//     1.148 ms, d = 64 within 1%.  d = 256 keeps its Q operand in registers at two waves per SIMD.
-//     The causal kernels, whose row sum takes 12 fewer registers (below), hold it in registers too,
-//     still at three waves per SIMD (four at d = 64: 120 registers); bit-identical, 4 × 32 × 8192:
-//     d = 64 0.744 → 0.733 ms, d = 128 1.144 → 1.119, d = 96 unchanged.  The non-causal kernels
-//     need the room.
+//   * Three waves per SIMD at d ≤ 128 (at most 168 registers; four at d = 64, 121 registers), two at
+//     d = 256: one score tile is live at a time (the next tile's scores are formed after the
+//     exponentials of the current one have read it), and the row sum takes 4 accumulator registers;
+//     the Q operand stays in registers.  Measured on MI355X (bit-identical outputs, causal 4 × 32 ×
+//     8192): one live score tile at three waves against two tiles at two waves, d = 128 1.345 →
+//     1.274 ms, d = 96 1.212 → 1.148 (Q then read from LDS to make room); Q back in registers once
+//     the row sum had freed 12 registers, d = 64 0.744 → 0.733, d = 128 1.144 → 1.119.
+//   * Without the causal mask every wave takes every tile, and the compiler would drop the per-tile
+//     `j < wave_tiles` test and schedule the two unrolled tiles as one block, at up to 168 registers
+//     with spills; an opaque tile count keeps the test, and the non-causal kernels compile to the
+//     causal ones' register counts (2 × 16 × 4096 non-causal, bit-identical: d = 64 0.137 → 0.132 ms,
+//     d = 96 0.170 → 0.161, d = 128 0.186 → 0.180, d = 256 0.436 → 0.424).
 //   * Head dims: Sᵀ takes D/64 k-steps of 64, Oᵀ D/32 column blocks of 32.  d = 96 uses the d = 128
 //     LDS rows: the DMA fills bytes 96..127 of each K and V row with zeros and the Q operand's last
 //     32 columns are zero, so the second k-step adds nothing, and only three V column blocks are read.
@@ -111,11 +109,6 @@ __global__ __launch_bounds__(kThreads, D <= 128 ? 3 : 2) void fwd_fp8_kernel(
   __shared__ __attribute__((aligned(1024))) uint8_t k1s[kBC * LR];
   __shared__ __attribute__((aligned(1024))) uint8_t v0s[kBC * LR];
   __shared__ __attribute__((aligned(1024))) uint8_t v1s[kBC * LR];
-  // The workgroup's Q rows (non-causal, d ≤ 128): B-operand fragments are read from here each tile
-  // instead of being held in registers, which keeps the kernel within three waves per SIMD (four at
-  // d = 64).
-  constexpr bool QLDS = D <= 128 && !CAUSAL;
-  __shared__ __attribute__((aligned(1024))) uint8_t qs[QLDS ? kBR * LR : 16];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -154,22 +147,19 @@ __global__ __launch_bounds__(kThreads, D <= 128 ? 3 : 2) void fwd_fp8_kernel(
   const auto mv = make_rsrc(V + head, head_bytes);
   const TileCopy<LR, kBC, kThreads, D> copy(tid, [](int r) { return swz8<LR>(r); });
 
-  // Qᵀ operand (B) in registers (causal, and d = 256): this lane's query, k-step s covers
-  // d = 64s + 32g .. +31.  Columns past D (d = 96: s = 1, g = 1) are read from an offset past the
-  // buffer's range (per-head bytes stay below 2^31), which returns zeros.  Otherwise the same
-  // fragments are read from the Q rows in LDS, whose columns past D the copy fills with zeros.
-  i32x8 qf[QLDS ? 1 : KS];
-  if constexpr (!QLDS) {
+  // Qᵀ operand (B) in registers: this lane's query, k-step s covers d = 64s + 32g .. +31.  Columns
+  // past D (d = 96: s = 1, g = 1) are read from an offset past the buffer's range (per-head bytes
+  // stay below 2^31), which returns zeros rather than the next row's codes.
+  i32x8 qf[KS];
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      uint32_t off = (uint32_t)(qi * D + 64 * s + 32 * g);
-      if constexpr (D == 96) {
-        if (s == 1 && g == 1) off = 0x80000000u;
-      }
-      const u32x4 lo = buf_load16(rq, off), hi = buf_load16(rq, off + 16);
-      qf[s] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
-                    (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+  for (int s = 0; s < KS; ++s) {
+    uint32_t off = (uint32_t)(qi * D + 64 * s + 32 * g);
+    if constexpr (D == 96) {
+      if (s == 1 && g == 1) off = 0x80000000u;
     }
+    const u32x4 lo = buf_load16(rq, off), hi = buf_load16(rq, off + 16);
+    qf[s] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                  (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
   }
   // Per-lane LDS offsets.  K rows (A operand): row perm23(lc) (+32 per key block), chunks 4s+2g+h.
   uint32_t koff[KS][2];
@@ -180,16 +170,6 @@ __global__ __launch_bounds__(kThreads, D <= 128 ? 3 : 2) void fwd_fp8_kernel(
 #pragma unroll
       for (int h = 0; h < 2; ++h)
         koff[s][h] = (uint32_t)(r * LR + 16 * ((4 * s + 2 * g + h) ^ swz8<LR>(r)));
-  }
-  // Q rows (QLDS): this lane's query row 32·wave + lc, chunks 4s + 2g + h (the K tiles' swizzle).
-  uint32_t qoff[KS][2];
-  {
-    const int r = 32 * wave + lc;
-#pragma unroll
-    for (int s = 0; s < KS; ++s)
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-        qoff[s][h] = (uint32_t)(r * LR + 16 * ((4 * s + 2 * g + h) ^ swz8<LR>(r)));
   }
   // V transposed reads: the 16-lane group's lane i = 2a + b reads row k0 + a, bytes n0 + 8b .. +7
   // with k0 = 16c + 8g and n0 = 128·half + 32db + 16·((lane >> 4) & 1); the lane receives column
@@ -203,12 +183,10 @@ __global__ __launch_bounds__(kThreads, D <= 128 ? 3 : 2) void fwd_fp8_kernel(
       voff[db] = (uint32_t)(r * LR + 16 * ((2 * (db + DB * half) + u) ^ swz8<LR>(r)) + 8 * b);
   }
 
-  const int wave_tiles = CAUSAL ? min(t_end, (qw + 31) / kBC + 1) : t_end;
+  int wave_tiles = CAUSAL ? min(t_end, (qw + 31) / kBC + 1) : t_end;
+  // Opaque without the mask, so that the per-tile test stays (see the header's non-causal note).
+  if constexpr (!CAUSAL) asm volatile("" : "+s"(wave_tiles));
 
-  if constexpr (QLDS) {
-    const TileCopy<LR, kBR, kThreads, D> copy_q(tid, [](int r) { return swz8<LR>(r); });
-    copy_q(rq, q0, qs);
-  }
   copy(mk, t_beg * kBC, k0s);
   if (t_beg + 1 < t_end) copy(mk, (t_beg + 1) * kBC, k1s);
   copy(mv, t_beg * kBC, v0s);
@@ -222,15 +200,7 @@ __global__ __launch_bounds__(kThreads, D <= 128 ? 3 : 2) void fwd_fp8_kernel(
       for (int r = 0; r < 16; ++r) acc[kb][r] = 0.f;
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
-      i32x8 qv;
-      if constexpr (QLDS) {
-        const u32x4 lo = *(const u32x4*)(qs + qoff[s][0]);
-        const u32x4 hi = *(const u32x4*)(qs + qoff[s][1]);
-        qv = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
-                   (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-      } else {
-        qv = qf[s];
-      }
+      const i32x8 qv = qf[s];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         const u32x4 lo = *(const u32x4*)(klds + koff[s][0] + kb * 32 * LR);
@@ -248,24 +218,22 @@ __global__ __launch_bounds__(kThreads, D <= 128 ? 3 : 2) void fwd_fp8_kernel(
 
   float m = -INFINITY;
   // Row-sum accumulator: register 0 of every lane holds Σ P of the lane's query (see above).
-  constexpr bool RS16 = CAUSAL;
-  constexpr int LN = RS16 ? 4 : 16;
   f32x16 oacc[DB];
-  std::conditional_t<RS16, f32x4, f32x16> lacc;
+  f32x4 lacc;
 #pragma unroll
   for (int b = 0; b < DB; ++b)
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[b][r] = 0.f;
 #pragma unroll
-  for (int r = 0; r < LN; ++r) lacc[r] = 0.f;
-  // 32×32×64 form: all-ones A operand, so every row of the output is the column sum of Pᵀ, i.e.
-  // each lane's accumulator holds its own query's sum.  16×16×128 form: lane l of the A operand is
-  // row l % 16, k-group l / 16, and lane l of Pᵀ is column l % 16, k-group l / 16, holding query
-  // l % 32 (k-groups 0 and 2 hold queries 0..15, groups 1 and 3 queries 16..31).  Output row i
-  // lands in lanes 16(i / 4) + j, register i % 4.  Rows 0 and 8 select groups 0 and 2, rows 4 and
-  // 12 groups 1 and 3: register 0 of lane l is then the sum of query l % 32, as in the other form.
-  const int one = RS16 ? ((lane & 3) == 0 && ((lane >> 2) & 1) == ((lane >> 4) & 1) ? 0x38383838 : 0)
-                       : 0x38383838;  // e4m3 1.0 or 0
+  for (int r = 0; r < 4; ++r) lacc[r] = 0.f;
+  // 16×16×128 product: lane l of the A operand is row l % 16, k-group l / 16, and lane l of Pᵀ is
+  // column l % 16, k-group l / 16, holding query l % 32 (k-groups 0 and 2 hold queries 0..15,
+  // groups 1 and 3 queries 16..31).  Output row i lands in lanes 16(i / 4) + j, register i % 4.
+  // Rows 0 and 8 select groups 0 and 2, rows 4 and 12 groups 1 and 3: register 0 of lane l is then
+  // the sum of query l % 32.
+  const int one = (lane & 3) == 0 && ((lane >> 2) & 1) == ((lane >> 4) & 1)
+                      ? 0x38383838  // e4m3 1.0
+                      : 0;
   const i32x8 sel = {one, one, one, one, one, one, one, one};
 
   auto tile = [&](auto parity, int j) {
@@ -307,7 +275,7 @@ __global__ __launch_bounds__(kThreads, D <= 128 ? 3 : 2) void fwd_fp8_kernel(
 #pragma unroll
           for (int r = 0; r < 16; ++r) oacc[b][r] *= alpha;
 #pragma unroll
-        for (int r = 0; r < LN; ++r) lacc[r] *= alpha;
+        for (int r = 0; r < 4; ++r) lacc[r] *= alpha;
         m = m_new;
       }
       const float m_off = (m == -INFINITY ? 0.f : m) - kPExp;  // P = 2^(s·c − m + kPExp)
@@ -339,8 +307,7 @@ __global__ __launch_bounds__(kThreads, D <= 128 ? 3 : 2) void fwd_fp8_kernel(
         oacc[db] = mfma_f8(vf, pf, oacc[db]);
       }
       // Σ over the tile's keys of the rounded P, in register 0 of each lane
-      if constexpr (RS16) lacc = mfma_f8_16(sel, pf, lacc);
-      else lacc = mfma_f8(sel, pf, lacc);
+      lacc = mfma_f8_16(sel, pf, lacc);
     }
     wait_vmem_all();
     __syncthreads();

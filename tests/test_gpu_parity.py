@@ -793,15 +793,14 @@ def test_fp8_other_head_dims_row0_exact(d):
 @pytest.mark.parametrize("causal", [False, True])
 def test_fp8_query_rows_independent(d, causal):
     """A NaN code in one query row stays within that row's wave of 32 queries.  At d = 96 each Q
-    row's 96 bytes are followed in memory by the next row, and the Q operand's last 32 columns must
-    come in as zeros (the causal kernels hold Q in registers, the others read it from the
-    zero-padded LDS rows), not as the next row's codes: those would meet K's zero padding, and
-    NaN · 0 would carry the NaN into the row before.  The NaN row (96) starts a wave, so the row
-    before it (95) belongs to another wave, and every wave but the NaN row's is bit for bit that of
-    the same call without the NaN.  Within the NaN row's own wave no more is promised: the reference
-    maximum is raised by a wave-wide vote, and the causal kernels' row-sum product multiplies each
-    query's P by the selector's zeros in the lanes of its partner query (l ± 16), so a NaN can reach
-    that partner's row sum."""
+    row's 96 bytes are followed in memory by the next row, and the Q operand's last 32 columns,
+    held in registers, must come in as zeros, not as the next row's codes: those would meet K's
+    zero padding, and NaN · 0 would carry the NaN into the row before.  The NaN row (96) starts a
+    wave, so the row before it (95) belongs to another wave, and every wave but the NaN row's is bit
+    for bit that of the same call without the NaN.  Within the NaN row's own wave no more is
+    promised: the reference maximum is raised by a wave-wide vote, and the row-sum product
+    multiplies each query's P by the selector's zeros in the lanes of its partner query (l ± 16), so
+    a NaN can reach that partner's row sum."""
     B, H, N = 1, 2, 200
     inp = _fp8_case(B, H, N, seed=500 + d + int(causal), d=d)
     scale = 1.0 / math.sqrt(d)
