@@ -55,7 +55,7 @@ def _case(i):
     return B, H, N, d, causal, scale
 
 
-CASES = [_case(i) for i in range(24)]
+CASES = [_case(i) for i in range(64)]
 
 
 @pytest.mark.parametrize("case", range(len(CASES)))
