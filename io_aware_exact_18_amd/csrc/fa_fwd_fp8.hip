@@ -41,10 +41,15 @@
 //   * Head dims: Sᵀ takes D/64 k-steps of 64, Oᵀ D/32 column blocks of 32.  d = 96 uses the d = 128
 //     LDS rows: the DMA fills bytes 96..127 of each K and V row with zeros and the Q operand's last
 //     32 columns are zero, so the second k-step adds nothing, and only three V column blocks are read.
-//   * d = 256: two workgroups per query tile, one per 128-column half of O.  Each forms the full Sᵀ
-//     (four k-steps) and the same P, and accumulates only its half of Oᵀ, so the state per wave stays
-//     that of d = 128.  Sᵀ is computed twice: 1.5× the matrix-core work of one pass.  The two halves
-//     are adjacent work items, so they run on one XCD and share its L2 for K and V.
+//   * d = 256: one workgroup per query tile holds the whole 32 × 256 Oᵀ accumulator per wave (245
+//     registers, two waves per SIMD), which fits since the row sum and Q layout changes above.  Grids
+//     of at most 256 query tiles, which leave half the compute units' slots empty, run two workgroups
+//     per query tile instead (CS = 2), one per 128-column half of O: each forms the full Sᵀ and the
+//     same P and accumulates only its half, 0.76× the matrix-core work of one pass on twice the work
+//     items.  The halves are adjacent work items, so they share one XCD's L2 for K and V.  Measured on
+//     MI355X (bit-identical outputs), one workgroup against two per query tile: causal 4 × 16 × 8192
+//     1.798 → 1.117 ms, non-causal 2 × 16 × 4096 0.464 → 0.297 ms; causal 1 × 3 × 1000 (24 query
+//     tiles) 0.033 → 0.039 ms, hence the rule.
 #include "fa_common.h"
 #include "fa_launch.h"
 
@@ -59,9 +64,9 @@ constexpr int kThreads = 256;
 // Bytes per K/V row in LDS (one e4m3 byte per element; d = 96 is padded to 128).
 template <int D>
 constexpr int lds_row() { return D == 96 ? 128 : D; }
-// Workgroups per query tile (column halves of O).
-template <int D>
-constexpr int col_splits() { return D == 256 ? 2 : 1; }
+// Workgroups per query tile (column halves of O) at d = 256: two when the grid has at most this many
+// query tiles, one otherwise (see the header).
+constexpr uint32_t kColSplitMaxTiles = 256;
 // P is formed as 2^(s·c − m + kPExp) against a per-row reference maximum m that is raised only when
 // some row of the wave sees a score more than kSlack above it, so P ≤ 2^(kPExp + kSlack) = 256 fits
 // e4m3 (largest finite 448) and the accumulators are rescaled on few tiles instead of most.
@@ -95,16 +100,17 @@ __device__ inline u32x2 lds_read_tr8(const uint8_t* p) {
   return __builtin_bit_cast(u32x2, r);
 }
 
-template <int D, bool CAUSAL, bool SPLIT>
+template <int D, bool CAUSAL, bool SPLIT, int CS>
 __global__ __launch_bounds__(kThreads, D <= 128 ? 3 : 2) void fwd_fp8_kernel(
     const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K, const uint8_t* __restrict__ V,
     bf16* __restrict__ O, float* __restrict__ LSE, int N, int nqt, float c_log2, float v_descale,
     int remap, SplitOut so) {
-  static_assert(!SPLIT || col_splits<D>() == 1, "the key-range split runs d ≤ 128");
+  static_assert(!SPLIT || D <= 128, "the key-range split runs d ≤ 128");
+  static_assert(CS == 1 || (CS == 2 && D == 256), "column halves only at d = 256");
   static_assert(D == 64 || D == 96 || D == 128 || D == 256, "head dims of the fp8 forward");
   constexpr int LR = lds_row<D>();
   constexpr int KS = LR / 64;                   // k-steps of Sᵀ
-  constexpr int DB = D / 32 / col_splits<D>();  // column blocks of Oᵀ per workgroup
+  constexpr int DB = D / 32 / CS;  // column blocks of Oᵀ per workgroup
   __shared__ __attribute__((aligned(1024))) uint8_t k0s[kBC * LR];
   __shared__ __attribute__((aligned(1024))) uint8_t k1s[kBC * LR];
   __shared__ __attribute__((aligned(1024))) uint8_t v0s[kBC * LR];
@@ -123,10 +129,10 @@ __global__ __launch_bounds__(kThreads, D <= 128 ? 3 : 2) void fwd_fp8_kernel(
     sg = (int)(logical / per_seg);
     logical %= per_seg;
   }
-  const int half = col_splits<D>() == 2 ? (int)(logical & 1u) : 0;  // column half of O (d = 256)
-  const uint32_t item = col_splits<D>() == 2 ? logical >> 1 : logical;
+  const int half = CS == 2 ? (int)(logical & 1u) : 0;  // column half of O (d = 256)
+  const uint32_t item = CS == 2 ? logical >> 1 : logical;
   int bh, qt;
-  head_tile(item, nqt, SPLIT ? so.bh_count : (int)(gridDim.x / col_splits<D>() / nqt), remap,
+  head_tile(item, nqt, SPLIT ? so.bh_count : (int)(gridDim.x / CS / nqt), remap,
             D <= 128 ? 3 : 2, bh, qt);
   if (CAUSAL) qt = nqt - 1 - qt;
   const int q0 = qt * kBR;
@@ -363,13 +369,13 @@ hipError_t launch(const Fp8FwdArgs& a, hipStream_t stream) {
   const int nqt = (a.N + kBR - 1) / kBR;
   const float c_log2 = a.scale * a.q_descale * a.k_descale * kLog2e;
   const uint32_t bh = (uint32_t)a.B * a.H;
-  if constexpr (col_splits<D>() == 1) {
+  if constexpr (D <= 128) {
     // Key-range split (the bf16 forward's rule and merge; fwd_split in fa_launch.h).
     const FwdSplit sp = a.workspace ? fwd_split(a.B, a.H, a.N, D, CAUSAL ? 1 : 0) : FwdSplit{0, 1};
     if (sp.nseg > 1) {
       SplitOut so{(float*)a.workspace, nullptr, sp.seg, (int)bh};
       so.part_ml = so.part_o + (size_t)sp.nseg * bh * a.N * D;
-      hipLaunchKernelGGL((fwd_fp8_kernel<D, CAUSAL, true>), dim3((uint32_t)sp.nseg * bh * nqt),
+      hipLaunchKernelGGL((fwd_fp8_kernel<D, CAUSAL, true, 1>), dim3((uint32_t)sp.nseg * bh * nqt),
                          dim3(kThreads), 0, stream, (const uint8_t*)a.q8, (const uint8_t*)a.k8,
                          (const uint8_t*)a.v8, (bf16*)a.o, a.lse, a.N, nqt, c_log2, a.v_descale, 0,
                          so);
@@ -379,9 +385,19 @@ hipError_t launch(const Fp8FwdArgs& a, hipStream_t stream) {
                               sp.seg, stream);
     }
   }
-  const uint32_t total = bh * nqt * col_splits<D>();
+  const int cs = (D == 256 && bh * (uint32_t)nqt <= kColSplitMaxTiles) ? 2 : 1;
+  const uint32_t total = bh * nqt * cs;
   const int remap = use_xcd_order(total, (long)bh, CAUSAL ? 1 : 0);
-  hipLaunchKernelGGL((fwd_fp8_kernel<D, CAUSAL, false>), dim3(total), dim3(kThreads), 0, stream,
+  if constexpr (D == 256) {
+    if (cs == 2) {
+      hipLaunchKernelGGL((fwd_fp8_kernel<D, CAUSAL, false, 2>), dim3(total), dim3(kThreads), 0,
+                         stream, (const uint8_t*)a.q8, (const uint8_t*)a.k8, (const uint8_t*)a.v8,
+                         (bf16*)a.o, a.lse, a.N, nqt, c_log2, a.v_descale, remap,
+                         SplitOut{nullptr, nullptr, 0, 0});
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((fwd_fp8_kernel<D, CAUSAL, false, 1>), dim3(total), dim3(kThreads), 0, stream,
                      (const uint8_t*)a.q8, (const uint8_t*)a.k8, (const uint8_t*)a.v8, (bf16*)a.o,
                      a.lse, a.N, nqt, c_log2, a.v_descale, remap, SplitOut{nullptr, nullptr, 0, 0});
   return hipGetLastError();

@@ -135,3 +135,36 @@ def test_fp8_grid_order_every_head(H):
                                                               int(err.max(axis=1).argmax()))
         worst = max(worst, float(err.max()))
     print(f"PARITY fp8 grid order H={H}: O {worst:.3g}")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp8_d256_column_split_rule(causal):
+    """The FP8 forward at d = 256 runs one workgroup per query tile on grids of more than 256 query
+    tiles and two (one per column half of O) on smaller ones.  2 × 9 heads of 2048 keys (288 query
+    tiles) take the first form; each head computed alone (16 tiles) takes the second.  Both must
+    give the same bits, and every head must match the oracle on the dequantised inputs at 6e-2
+    plus half a bf16 ulp of O*."""
+    import workloads
+    B, H, N, d = 2, 9, 2048, 256
+    scale = 1.0 / np.sqrt(d)
+    g = torch.Generator().manual_seed(33000 + int(causal))
+    inp = {}
+    for name in "qkv":
+        x = torch.randn(B, H, N, d, generator=g)
+        inp[name + "8"], inp["s" + name] = workloads.quantize_e4m3(x)
+    codes = [inp[n + "8"].cuda() for n in "qkv"]
+    o8, l8 = fa().fwd_fp8(*codes, inp["sq"], inp["sk"], inp["sv"], causal, scale)
+    torch.cuda.synchronize()
+    deq = [workloads.dequantized64(inp[n + "8"], inp["s" + n]) for n in "qkv"]
+    worst = 0.0
+    for h in range(B * H):
+        b, hh = divmod(h, H)
+        one = [c[b:b + 1, hh:hh + 1].contiguous() for c in codes]
+        o1, l1 = fa().fwd_fp8(*one, inp["sq"], inp["sk"], inp["sv"], causal, scale)
+        torch.cuda.synchronize()
+        assert torch.equal(o1[0, 0], o8[b, hh]) and torch.equal(l1[0, 0], l8[b, hh]), (causal, h)
+        o_ref, _ = oracle.attention_head_fwd64(*(x[b, hh].numpy() for x in deq), causal, scale)
+        err = np.abs(_np64(o8[b, hh]) - o_ref)
+        assert np.all(err <= 6e-2 + _half_ulp_bf16(o_ref)), (causal, h, float(err.max()))
+        worst = max(worst, float(err.max()))
+    print(f"PARITY fp8 d=256 column-split rule causal={causal}: O {worst:.3g}")
