@@ -137,17 +137,19 @@ def test_fp8_grid_order_every_head(H):
     print(f"PARITY fp8 grid order H={H}: O {worst:.3g}")
 
 
+@pytest.mark.parametrize("B,H,N", [(2, 9, 2048), (3, 11, 1000)])
 @pytest.mark.parametrize("causal", [False, True])
-def test_fp8_d256_column_split_rule(causal):
+def test_fp8_d256_column_split_rule(B, H, N, causal):
     """The FP8 forward at d = 256 runs one workgroup per query tile on grids of more than 256 query
     tiles and two (one per column half of O) on smaller ones.  2 × 9 heads of 2048 keys (288 query
-    tiles) take the first form; each head computed alone (16 tiles) takes the second.  Both must
-    give the same bits, and every head must match the oracle on the dequantised inputs at 6e-2
-    plus half a bf16 ulp of O*."""
+    tiles) and 3 × 11 heads of 1000 keys (264 tiles, the last one of each head ragged) take the
+    first form; each head computed alone (16 or 8 tiles) takes the second.  Both must give the same
+    bits, and every head must match the oracle on the dequantised inputs at 6e-2 plus half a bf16
+    ulp of O*."""
     import workloads
-    B, H, N, d = 2, 9, 2048, 256
+    d = 256
     scale = 1.0 / np.sqrt(d)
-    g = torch.Generator().manual_seed(33000 + int(causal))
+    g = torch.Generator().manual_seed(33000 + N + int(causal))
     inp = {}
     for name in "qkv":
         x = torch.randn(B, H, N, d, generator=g)
